@@ -1,0 +1,657 @@
+/*
+ * oracle.c -- plain, slow, single-threaded, fp64 CPU oracle of the speculative
+ * verification step: token-tree build, tree-masked attention, acceptance /
+ * selection / resampling, and the KV commit of the accepted path.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the package smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no source, header,
+ * table or helper with the HIP library, and neither one includes the other.
+ *
+ * Sources (web pages; cited by page title and section):
+ *   [ReDrafter] "Recurrent Drafter for Fast Speculative Decoding in Large
+ *               Language Models": sections "Dynamic Tree Attention" and
+ *               "The Full Speculative Decoding Loop" (Steps 3-6).
+ *   [Clover]    "Clover: Regressive Lightweight Speculative Decoding with
+ *               Sequential Knowledge": section "Inference-Time Verification:
+ *               Token Tree Construction and Tree Attention" (mask, Figure 4).
+ *   [ResiSpec]  paperpeel 2608.24411 (residual drift in multi-candidate
+ *               verification): section 4 (residual distribution, sequential
+ *               verification of N candidates), Appendix B.1 (path marginals).
+ *
+ * Conventions (readings where the pages are silent; each one is listed in the
+ * design notes of the repository):
+ *   - Tree position 0 is the root: the last token already sampled by the target,
+ *     whose K/V are not cached yet.  Draft nodes are 1..T-1; T = n_nodes[b]
+ *     counts the root.
+ *   - Beams are numbered into the tree in beam-major order of first appearance.
+ *   - The attention mask of node i holds i itself, the root and every ancestor.
+ *   - Target row t is the target distribution for the children of node t (and
+ *     for the bonus token after t); dft_row[t] names the draft row the children
+ *     of t were drawn from.
+ *   - Padding: parent/token/depth = -1 and an all-zero mask for t >= T.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_OK 0
+#define ORC_ERR -1
+
+#define ORC_GREEDY 0
+#define ORC_REJECT_PATH 1
+#define ORC_REJECT_RECURSIVE 2
+
+/* |ratio - u| below this counts as a decision near-tie (both sides count). */
+#define ORC_NEAR_TIE 1e-5
+/* A running-sum boundary within this distance of the threshold u * total of an
+ * inverse-CDF draw from a normalised distribution counts as a sampling near-tie. */
+#define ORC_CDF_NEAR_TIE 1e-9
+
+/* ------------------------------------------------------------------------ */
+/* small helpers                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 -> double, exact: a bf16 is the top 16 bits of an IEEE binary32. */
+static double bf16_to_double(uint16_t h)
+{
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double load_elem(int dtype, const void *base, size_t idx)
+{
+    if (dtype == 0) return (double)((const float *)base)[idx];
+    return bf16_to_double(((const uint16_t *)base)[idx]);
+}
+
+static int anc_has(const uint64_t *row, int a)
+{
+    return (int)((row[a >> 6] >> (a & 63)) & 1u);
+}
+
+static void anc_set(uint64_t *row, int a)
+{
+    row[a >> 6] |= (uint64_t)1 << (a & 63);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 1. Tree construction                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Finish a tree whose parent[] and token[] are filled for nodes 0..T-1:
+ * depth by walking to the root, ancestor mask = self + every ancestor + root
+ * ([Clover] tree mask: M_ij = 1 iff j is an ancestor of i or i = j). */
+static void finish_tree(int T, int T_cap, int n_words, int32_t *parent, int32_t *depth,
+                        uint64_t *anc, int32_t *token)
+{
+    for (int t = 0; t < T_cap; ++t) {
+        uint64_t *row = anc + (size_t)t * n_words;
+        for (int w = 0; w < n_words; ++w) row[w] = 0;
+        if (t >= T) {
+            parent[t] = -1;
+            token[t] = -1;
+            depth[t] = -1;
+            continue;
+        }
+        int d = 0;
+        int cur = t;
+        anc_set(row, t);
+        while (cur != 0) {
+            cur = parent[cur];
+            anc_set(row, cur);
+            ++d;
+        }
+        depth[t] = d;
+    }
+}
+
+/*
+ * Beams -> token tree ([ReDrafter] "Dynamic Tree Attention": candidates share
+ * prefixes; the packed beam keeps each distinct prefix once, and the mask lets a
+ * token see only its own prefix).  Written as a textbook trie insertion: walk
+ * each beam from the root, reuse the child that carries the same token, else
+ * append a new node.  Node ids are given in beam-major order of first
+ * appearance.  beam_node[i][k] = node holding beam i's prefix of length k+1.
+ *
+ * Layout: beams [B][W][L], root_token [B]; outputs n_nodes [B], parent/token/
+ * depth [B][T_cap], anc [B][T_cap][ceil(T_cap/64)], beam_node [B][W][L] (or NULL).
+ */
+int orc_build_tree_beams(int B, int W, int L, int T_cap, const int32_t *beams,
+                         const int32_t *root_token, int32_t *n_nodes, int32_t *parent,
+                         int32_t *token, int32_t *depth, uint64_t *anc, int32_t *beam_node)
+{
+    if (B < 0 || W < 1 || L < 1 || T_cap < 1 + W * L) return ORC_ERR;
+    int n_words = (T_cap + 63) / 64;
+    for (int b = 0; b < B; ++b) {
+        int32_t *par = parent + (size_t)b * T_cap;
+        int32_t *tok = token + (size_t)b * T_cap;
+        int T = 1;
+        par[0] = -1;
+        tok[0] = root_token[b];
+        for (int i = 0; i < W; ++i) {
+            int cur = 0;
+            for (int k = 0; k < L; ++k) {
+                int32_t x = beams[((size_t)b * W + i) * L + k];
+                int child = -1;
+                for (int c = 1; c < T; ++c) {
+                    if (par[c] == cur && tok[c] == x) {
+                        child = c;
+                        break;
+                    }
+                }
+                if (child < 0) {
+                    child = T++;
+                    par[child] = cur;
+                    tok[child] = x;
+                }
+                if (beam_node) beam_node[((size_t)b * W + i) * L + k] = child;
+                cur = child;
+            }
+        }
+        n_nodes[b] = T;
+        finish_tree(T, T_cap, n_words, par, depth + (size_t)b * T_cap,
+                    anc + (size_t)b * T_cap * n_words, tok);
+    }
+    return ORC_OK;
+}
+
+/*
+ * Explicit candidate tree (static trees of parallel heads, [Clover] "Token tree
+ * construction"; caterpillars of i.i.d. candidates, [ResiSpec] section 4).
+ * Candidate j (0-based) becomes node j+1; cand_parent[j] is its parent's tree
+ * index and must lie in [0, j].  Duplicate siblings are kept as given.
+ * A sequence whose parent list is not topological becomes a root-only tree and
+ * its bad flag is set.
+ */
+int orc_build_tree_explicit(int B, int N, int T_cap, const int32_t *cand_parent,
+                            const int32_t *cand_token, const int32_t *root_token,
+                            int32_t *n_nodes, int32_t *parent, int32_t *token, int32_t *depth,
+                            uint64_t *anc, int32_t *bad)
+{
+    if (B < 0 || N < 0 || T_cap < 1 + N) return ORC_ERR;
+    int n_words = (T_cap + 63) / 64;
+    for (int b = 0; b < B; ++b) {
+        int32_t *par = parent + (size_t)b * T_cap;
+        int32_t *tok = token + (size_t)b * T_cap;
+        int ok = 1;
+        for (int j = 0; j < N; ++j) {
+            int32_t p = cand_parent[(size_t)b * N + j];
+            if (p < 0 || p > j) ok = 0;
+        }
+        int T = ok ? N + 1 : 1;
+        par[0] = -1;
+        tok[0] = root_token[b];
+        for (int j = 0; j < T - 1; ++j) {
+            par[j + 1] = cand_parent[(size_t)b * N + j];
+            tok[j + 1] = cand_token[(size_t)b * N + j];
+        }
+        n_nodes[b] = T;
+        if (bad) bad[b] = !ok;
+        finish_tree(T, T_cap, n_words, par, depth + (size_t)b * T_cap,
+                    anc + (size_t)b * T_cap * n_words, tok);
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2. Tree-masked attention                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * One output row of tree attention ([ReDrafter] Step 4: one forward pass over
+ * the packed beam under the tree mask, each token attending only to its own
+ * prefix; [Clover] mask M_ij).  Query (b, t, h) attends to every context key
+ * 0..ctx-1 and to the tree keys ctx+a for every a in mask(t) (self, ancestors,
+ * root).  Scores are q.k * scale; softmax with max subtraction; all in fp64.
+ * Query head h reads KV head h / (H / Hkv).  Rows t >= T are zero.
+ *
+ * Layout: q [B][T_cap][H][D], k/v [B][Hkv][cap][D], out_row [D].
+ */
+static void attention_row(int dtype, int T_cap, int H, int Hkv, int D, int cap,
+                          const void *q, const void *kc, const void *vc, int ctx, int T,
+                          const uint64_t *anc_row, double scale, int b, int t, int h,
+                          double *out_row, double *score_buf)
+{
+    for (int d = 0; d < D; ++d) out_row[d] = 0.0;
+    if (t >= T) return;
+    int g = h / (H / Hkv);
+    size_t q_off = (((size_t)b * T_cap + t) * H + h) * D;
+    size_t kv_base = ((size_t)b * Hkv + g) * (size_t)cap * D;
+    int n_keys = ctx + T;
+    double m = -INFINITY;
+    for (int j = 0; j < n_keys; ++j) {
+        if (j >= ctx && !anc_has(anc_row, j - ctx)) {
+            score_buf[j] = -INFINITY;
+            continue;
+        }
+        double s = 0.0;
+        for (int d = 0; d < D; ++d)
+            s += load_elem(dtype, q, q_off + d) * load_elem(dtype, kc, kv_base + (size_t)j * D + d);
+        s *= scale;
+        score_buf[j] = s;
+        if (s > m) m = s;
+    }
+    double denom = 0.0;
+    for (int j = 0; j < n_keys; ++j) {
+        if (score_buf[j] == -INFINITY) continue;
+        double w = exp(score_buf[j] - m);
+        denom += w;
+        for (int d = 0; d < D; ++d)
+            out_row[d] += w * load_elem(dtype, vc, kv_base + (size_t)j * D + d);
+    }
+    for (int d = 0; d < D; ++d) out_row[d] /= denom;
+}
+
+/*
+ * Tree attention for a list of rows.  sel holds n_sel (b, t, h) triples; with
+ * sel == NULL every row of [B][T_cap][H] is computed in that order.  out is
+ * [n_rows][D] fp64.  scale <= 0 means 1/sqrt(D).  Returns ORC_ERR on bad
+ * shapes, or when ctx_len[b] + n_nodes[b] exceeds the cache capacity.
+ */
+int orc_tree_attention(int dtype, int B, int T_cap, int H, int Hkv, int D, int cap,
+                       const void *q, const void *kc, const void *vc, const int32_t *ctx_len,
+                       const int32_t *n_nodes, const uint64_t *anc, double scale, int n_sel,
+                       const int32_t *sel, double *out)
+{
+    if (B < 1 || T_cap < 1 || H < 1 || Hkv < 1 || H % Hkv != 0 || D < 1) return ORC_ERR;
+    if (scale <= 0.0) scale = 1.0 / sqrt((double)D);
+    int n_words = (T_cap + 63) / 64;
+    for (int b = 0; b < B; ++b)
+        if (ctx_len[b] < 0 || n_nodes[b] < 1 || n_nodes[b] > T_cap || ctx_len[b] + n_nodes[b] > cap)
+            return ORC_ERR;
+    size_t n_rows = sel ? (size_t)n_sel : (size_t)B * T_cap * H;
+    double *score_buf = (double *)malloc(sizeof(double) * ((size_t)cap + 1));
+    if (!score_buf) return ORC_ERR;
+    for (size_t r = 0; r < n_rows; ++r) {
+        int b, t, h;
+        if (sel) {
+            b = sel[3 * r];
+            t = sel[3 * r + 1];
+            h = sel[3 * r + 2];
+            if (b < 0 || b >= B || t < 0 || t >= T_cap || h < 0 || h >= H) {
+                free(score_buf);
+                return ORC_ERR;
+            }
+        } else {
+            b = (int)(r / ((size_t)T_cap * H));
+            t = (int)((r / H) % T_cap);
+            h = (int)(r % H);
+        }
+        attention_row(dtype, T_cap, H, Hkv, D, cap, q, kc, vc, ctx_len[b], n_nodes[b],
+                      anc + ((size_t)b * T_cap + t) * n_words, scale, b, t, h,
+                      out + r * D, score_buf);
+    }
+    free(score_buf);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 3. Verification                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Softmax of one logits row in fp64: p(v) = exp(l_v - max) / sum_v' exp(l_v' - max). */
+static void softmax_row(int V, const float *logits, double *p)
+{
+    double m = -INFINITY;
+    for (int v = 0; v < V; ++v)
+        if ((double)logits[v] > m) m = (double)logits[v];
+    double s = 0.0;
+    for (int v = 0; v < V; ++v) {
+        p[v] = exp((double)logits[v] - m);
+        s += p[v];
+    }
+    for (int v = 0; v < V; ++v) p[v] /= s;
+}
+
+/* Greedy target token: the first index holding the row maximum (ties go to
+ * the lowest index), decided on the fp32 logits themselves. */
+static int argmax_row(int V, const float *logits)
+{
+    int best = 0;
+    for (int v = 1; v < V; ++v)
+        if (logits[v] > logits[best]) best = v;
+    return best;
+}
+
+/* Unnormalised residual mass in closed form, Z(c) = sum_v max(0, p(v) - c q(v)).
+ * Used by the closed-form identity pin only (orc_residual_chain). */
+static double residual_mass(int V, const double *p, const double *q, double c)
+{
+    double z = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double w = p[v] - c * (q ? q[v] : 0.0);
+        if (w > 0.0) z += w;
+    }
+    return z;
+}
+
+/* One rejection ([ResiSpec] section 4): r <- max(0, r - q) / sum_v max(0, r - q).
+ * Returns the normaliser; when it is not positive r is left untouched. */
+static double residual_step(int V, double *r, const double *q)
+{
+    double z = 0.0;
+    for (int v = 0; v < V; ++v) {
+        double w = r[v] - q[v];
+        if (w > 0.0) z += w;
+    }
+    if (!(z > 0.0)) return z;
+    for (int v = 0; v < V; ++v) {
+        double w = r[v] - q[v];
+        r[v] = w > 0.0 ? w / z : 0.0;
+    }
+    return z;
+}
+
+/*
+ * Inverse-CDF draw from the distribution r (weights, summing to about one) in
+ * ascending vocabulary order: the smallest v whose running sum exceeds u * S,
+ * S being the total of r.  If rounding leaves no such v, the last v with
+ * positive weight.  *near is set when a running-sum boundary lies within
+ * ORC_CDF_NEAR_TIE of u * S.
+ */
+static int sample_inverse_cdf(int V, const double *r, double u, int *near)
+{
+    double total = 0.0;
+    for (int v = 0; v < V; ++v)
+        if (r[v] > 0.0) total += r[v];
+    double thr = u * total;
+    double run = 0.0;
+    int last_pos = -1;
+    *near = 0;
+    for (int v = 0; v < V; ++v) {
+        if (!(r[v] > 0.0)) continue;
+        last_pos = v;
+        double before = run;
+        run += r[v];
+        if (run > thr) {
+            if (fabs(run - thr) < ORC_CDF_NEAR_TIE || fabs(before - thr) < ORC_CDF_NEAR_TIE)
+                *near = 1;
+            return v;
+        }
+    }
+    return last_pos < 0 ? 0 : last_pos;
+}
+
+/*
+ * Verification of one packed tree per sequence.
+ *
+ * Rows: tgt [B][T_cap][V] fp32 target logits (row t = distribution after node
+ * t); dft [B][R][V] fp32 draft logits, dft_row [B][T_cap] (row the children of
+ * t were drawn from, -1 if none).  p_t = softmax(tgt[t]), q_t = softmax of the
+ * draft row of t.  Uniforms: u_node [B][T_cap] (one per node, index 0 unused),
+ * u_final [B].
+ *
+ * GREEDY ([ReDrafter] Step 5, token matches): node t is accepted iff its token
+ *   equals the argmax of its parent's target row.
+ * REJECT_PATH ([ReDrafter] Step 5, rejection sampling after Leviathan et al.):
+ *   node t is accepted iff u_node[t] < p_par(x) / q_par(x), independently per
+ *   node; a candidate stops at its first rejection.
+ * In both, a node is kept when it and all its ancestors are accepted; the
+ * longest kept prefix over all candidates wins ([ReDrafter] "What longest
+ * accepted prefix means"), ties going to the lowest node index (= lowest beam
+ * index).  At the stop node s the next token is argmax p_s (GREEDY); for
+ * REJECT_PATH it is drawn with u_final from norm(max(0, p_s - q_s)) when s has
+ * children (all rejected) and from p_s when s is a leaf.
+ * REJECT_RECURSIVE ([ResiSpec] section 4, sequential verification): walk from
+ *   the root; the children of s are checked in index order against the current
+ *   target p' (p' = p_s at first): accept child x iff u < p'(x)/q_s(x); on a
+ *   rejection p' <- norm(max(0, p' - q_s)).  An acceptance moves to that child
+ *   and restarts with p' = p_child.  When s has no child left, the next token
+ *   is drawn from p'.  p' is kept as an explicit normalised vector, renormalised
+ *   after every rejection exactly as the definition reads.  A rejection whose
+ *   residual has no positive mass (possible only through rounding) rejects the
+ *   remaining children and draws from p_s; it is counted in fallback[b].
+ *
+ * Outputs: acc_len [B] (depth of the stop node), acc_path [B][T_cap] (root
+ * first, -1 after the path), next_token [B], p_tok/q_tok [B][T_cap]
+ * (p_par(token), q_par(token); 0 for the root, padding, and q in GREEDY),
+ * decision [B][T_cap] (1 accepted, 0 rejected, -1 untested), near_tie [B]
+ * (decision near-ties |ratio - u| < 1e-5 plus a CDF near-tie), fallback [B].
+ */
+int orc_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, const float *dft,
+               const int32_t *dft_row, const int32_t *n_nodes, const int32_t *parent,
+               const int32_t *token, const int32_t *depth, const float *u_node,
+               const float *u_final, int32_t *acc_len, int32_t *acc_path, int32_t *next_token,
+               double *p_tok, double *q_tok, int8_t *decision, int32_t *near_tie,
+               int32_t *fallback)
+{
+    if (mode < ORC_GREEDY || mode > ORC_REJECT_RECURSIVE) return ORC_ERR;
+    if (B < 0 || T_cap < 1 || V < 1) return ORC_ERR;
+    if (mode != ORC_GREEDY && (!dft || !dft_row || R < 1)) return ORC_ERR;
+
+    double *p_rows = (double *)malloc(sizeof(double) * (size_t)T_cap * V);
+    double *q_rows = (double *)malloc(sizeof(double) * (size_t)T_cap * V);
+    int *has_q = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *acc = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *chain = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *n_child = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!p_rows || !q_rows || !has_q || !acc || !chain || !n_child || !r) {
+        free(p_rows); free(q_rows); free(has_q); free(acc); free(chain); free(n_child); free(r);
+        return ORC_ERR;
+    }
+    int rc = ORC_OK;
+
+    for (int b = 0; b < B && rc == ORC_OK; ++b) {
+        int T = n_nodes[b];
+        const int32_t *par = parent + (size_t)b * T_cap;
+        const int32_t *tok = token + (size_t)b * T_cap;
+        const int32_t *dep = depth + (size_t)b * T_cap;
+        const float *ub = u_node + (size_t)b * T_cap;
+        int32_t *path = acc_path + (size_t)b * T_cap;
+        int8_t *dec = decision + (size_t)b * T_cap;
+        double *pt = p_tok + (size_t)b * T_cap;
+        double *qt = q_tok + (size_t)b * T_cap;
+        if (T < 1 || T > T_cap) { rc = ORC_ERR; break; }
+
+        for (int t = 0; t < T_cap; ++t) {
+            path[t] = -1;
+            dec[t] = -1;
+            pt[t] = 0.0;
+            qt[t] = 0.0;
+            n_child[t] = 0;
+            has_q[t] = 0;
+        }
+        for (int t = 1; t < T; ++t) {
+            if (par[t] < 0 || par[t] >= t || tok[t] < 0 || tok[t] >= V) { rc = ORC_ERR; break; }
+            n_child[par[t]]++;
+        }
+        if (rc != ORC_OK) break;
+        near_tie[b] = 0;
+        fallback[b] = 0;
+
+        /* distributions of every node row */
+        for (int t = 0; t < T; ++t) {
+            softmax_row(V, tgt + ((size_t)b * T_cap + t) * V, p_rows + (size_t)t * V);
+            if (mode != ORC_GREEDY) {
+                int r = dft_row[(size_t)b * T_cap + t];
+                if (r >= 0 && r < R) {
+                    softmax_row(V, dft + ((size_t)b * R + r) * V, q_rows + (size_t)t * V);
+                    has_q[t] = 1;
+                } else if (n_child[t] > 0) {
+                    rc = ORC_ERR;
+                }
+            }
+        }
+        if (rc != ORC_OK) break;
+        for (int t = 1; t < T; ++t) {
+            pt[t] = p_rows[(size_t)par[t] * V + tok[t]];
+            if (mode != ORC_GREEDY) qt[t] = q_rows[(size_t)par[t] * V + tok[t]];
+        }
+
+        int stop = 0;
+
+        if (mode == ORC_GREEDY || mode == ORC_REJECT_PATH) {
+            for (int t = 1; t < T; ++t) {
+                if (mode == ORC_GREEDY) {
+                    acc[t] = tok[t] == argmax_row(V, tgt + ((size_t)b * T_cap + par[t]) * V);
+                } else {
+                    double ratio = qt[t] > 0.0 ? pt[t] / qt[t] : (pt[t] > 0.0 ? INFINITY : 0.0);
+                    double u = (double)ub[t];
+                    acc[t] = u < ratio;
+                    if (fabs(ratio - u) < ORC_NEAR_TIE) near_tie[b]++;
+                }
+                dec[t] = (int8_t)acc[t];
+            }
+            chain[0] = 1;
+            for (int t = 1; t < T; ++t) chain[t] = acc[t] && chain[par[t]];
+            for (int t = 1; t < T; ++t)
+                if (chain[t] && dep[t] > dep[stop]) stop = t;
+            if (mode == ORC_REJECT_PATH) {
+                /* draw from p_s, or from norm(max(0, p_s - q_s)) when every child of
+                 * the stop node was rejected */
+                memcpy(r, p_rows + (size_t)stop * V, sizeof(double) * (size_t)V);
+                if (n_child[stop] > 0 && !(residual_step(V, r, q_rows + (size_t)stop * V) > 0.0)) {
+                    fallback[b] = 1;
+                    memcpy(r, p_rows + (size_t)stop * V, sizeof(double) * (size_t)V);
+                }
+            }
+        } else {
+            /* sequential multi-candidate verification, residual renormalised after
+             * each rejection */
+            int s = 0;
+            for (;;) {
+                const double *q = has_q[s] ? q_rows + (size_t)s * V : NULL;
+                memcpy(r, p_rows + (size_t)s * V, sizeof(double) * (size_t)V);
+                int moved = 0, dead = 0;
+                for (int ch = s + 1; ch < T; ++ch) {
+                    if (par[ch] != s) continue;
+                    if (dead) {
+                        dec[ch] = 0;
+                        continue;
+                    }
+                    int x = tok[ch];
+                    double ratio = q[x] > 0.0 ? r[x] / q[x] : (r[x] > 0.0 ? INFINITY : 0.0);
+                    double u = (double)ub[ch];
+                    if (fabs(ratio - u) < ORC_NEAR_TIE) near_tie[b]++;
+                    if (u < ratio) {
+                        dec[ch] = 1;
+                        s = ch;
+                        moved = 1;
+                        break;
+                    }
+                    dec[ch] = 0;
+                    if (!(residual_step(V, r, q) > 0.0)) {
+                        dead = 1;
+                        fallback[b] = 1;
+                        memcpy(r, p_rows + (size_t)s * V, sizeof(double) * (size_t)V);
+                    }
+                }
+                if (moved) continue;
+                stop = s;
+                break;
+            }
+        }
+
+        acc_len[b] = dep[stop];
+        for (int cur = stop; cur >= 0; cur = par[cur]) path[dep[cur]] = cur;
+
+        if (mode == ORC_GREEDY) {
+            next_token[b] = argmax_row(V, tgt + ((size_t)b * T_cap + stop) * V);
+        } else {
+            int near = 0;
+            next_token[b] = sample_inverse_cdf(V, r, (double)u_final[b], &near);
+            near_tie[b] += near;
+        }
+    }
+    free(r);
+    free(p_rows); free(q_rows); free(has_q); free(acc); free(chain); free(n_child);
+    return rc;
+}
+
+/*
+ * Residual chain of one (p, q) pair, for pins of the closed form.
+ * literal = 0: closed form, c_0 = 0, Z_0 = 1, c_{k+1} = c_k + Z_k,
+ *   Z_{k+1} = sum max(0, p - c_{k+1} q); dist_k = max(0, p - c_k q) / Z_k.
+ * literal = 1: the definition iterated ([ResiSpec] section 4):
+ *   dist_0 = p, dist_{k+1} = max(0, dist_k - q) / sum max(0, dist_k - q).
+ * dist is [K+1][V]; mass (may be NULL) gets Z_k (closed form) or the
+ * normaliser of step k (literal, 1 for k = 0).  A zero normaliser stops the
+ * chain and leaves the later rows zero; the number of rows filled is returned.
+ */
+int orc_residual_chain(int V, const double *p, const double *q, int K, int literal,
+                       double *dist, double *mass)
+{
+    int filled = 0;
+    if (!literal) {
+        double c = 0.0, z = 1.0;
+        for (int k = 0; k <= K; ++k) {
+            if (k > 0) {
+                c += z;
+                z = residual_mass(V, p, q, c);
+            }
+            if (mass) mass[k] = z;
+            if (!(z > 0.0)) break;
+            for (int v = 0; v < V; ++v) {
+                double w = p[v] - c * q[v];
+                dist[(size_t)k * V + v] = w > 0.0 ? w / z : 0.0;
+            }
+            filled = k + 1;
+        }
+    } else {
+        for (int v = 0; v < V; ++v) dist[v] = p[v];
+        if (mass) mass[0] = 1.0;
+        filled = 1;
+        for (int k = 1; k <= K; ++k) {
+            double z = 0.0;
+            for (int v = 0; v < V; ++v) {
+                double w = dist[(size_t)(k - 1) * V + v] - q[v];
+                if (w > 0.0) z += w;
+            }
+            if (mass) mass[k] = z;
+            if (!(z > 0.0)) break;
+            for (int v = 0; v < V; ++v) {
+                double w = dist[(size_t)(k - 1) * V + v] - q[v];
+                dist[(size_t)k * V + v] = w > 0.0 ? w / z : 0.0;
+            }
+            filled = k + 1;
+        }
+    }
+    for (int k = filled; k <= K; ++k)
+        for (int v = 0; v < V; ++v) dist[(size_t)k * V + v] = 0.0;
+    return filled;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 4. KV commit                                                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Move the accepted path's K/V into contiguous cache slots ([ReDrafter] Step 6:
+ * accepted tokens are appended to the context and the next step starts from
+ * there).  For i = 1..acc_len: slot ctx + acc_path[i] -> slot ctx + i, for K and
+ * V of every KV head; the root stays at slot ctx.  All sources are read before
+ * any slot is written.  ctx_len[b] becomes ctx + acc_len + 1.
+ * elem_bytes is 2 (bf16) or 4 (fp32); caches are [B][Hkv][cap][D].
+ */
+int orc_kv_compact(int elem_bytes, int B, int Hkv, int D, int cap, int T_cap, uint8_t *kc,
+                   uint8_t *vc, int32_t *ctx_len, const int32_t *acc_len, const int32_t *acc_path)
+{
+    if (elem_bytes != 2 && elem_bytes != 4) return ORC_ERR;
+    size_t row = (size_t)D * elem_bytes;
+    uint8_t *tmp = (uint8_t *)malloc(row * (size_t)T_cap);
+    if (!tmp) return ORC_ERR;
+    for (int b = 0; b < B; ++b) {
+        int ctx = ctx_len[b];
+        int n = acc_len[b];
+        const int32_t *path = acc_path + (size_t)b * T_cap;
+        if (n < 0 || n >= T_cap || ctx + n + 1 > cap) { free(tmp); return ORC_ERR; }
+        for (int i = 1; i <= n; ++i)
+            if (path[i] < i || ctx + path[i] >= cap) { free(tmp); return ORC_ERR; }
+        for (int g = 0; g < Hkv; ++g) {
+            for (int which = 0; which < 2; ++which) {
+                uint8_t *base = (which ? vc : kc) + ((size_t)b * Hkv + g) * (size_t)cap * row;
+                for (int i = 1; i <= n; ++i)
+                    memcpy(tmp + (size_t)i * row, base + (size_t)(ctx + path[i]) * row, row);
+                for (int i = 1; i <= n; ++i)
+                    memcpy(base + (size_t)(ctx + i) * row, tmp + (size_t)i * row, row);
+            }
+        }
+        ctx_len[b] = ctx + n + 1;
+    }
+    free(tmp);
+    return ORC_OK;
+}

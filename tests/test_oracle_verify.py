@@ -1,0 +1,371 @@
+"""Pins of the oracle's verification against what the pages and the mathematics fix.
+
+- GREEDY equals a brute-force longest matching prefix over the beams (ReDrafter
+  page, Step 5: token matches, longest accepted prefix across candidates).
+- REJECT_PATH equals independent per-beam scans written with scipy's softmax
+  (a second formulation), including the residual draw at the stop node.
+- REJECT_RECURSIVE reproduces the target distribution: the exact path marginal
+  of the ResiSpec page's Appendix B.1 sums to p within 1e-12, the literal
+  iterated residual norm(max(0, p' - q)) equals the closed form, and 1e6 seeded
+  trials at V=16 pass a chi-square test for N in {1, 2, 4, 8} candidates.
+- Negative controls fail the same chi-square test: per-path rejection with two
+  or more i.i.d. siblings, and two Python mutants (resampling from p instead of
+  the residual; a residual that is never renormalised).
+- The first-candidate acceptance rate is sum_x min(p, q) = 1 - TV(p, q)
+  (drafter-history page, DSpark acceptance label) within 4 sigma.
+- Special cases: q = p always accepts the first candidate; a one-hot p makes
+  sequential rejection take the greedy path.
+"""
+import numpy as np
+import pytest
+from scipy import stats
+from scipy.special import softmax
+
+from tree_attention_verification_beam_amd import synth
+
+
+# ----------------------------------------------------------------------------
+# helpers
+# ----------------------------------------------------------------------------
+
+def _beam_case(oracle, seed, B, W, L, V, sigma=1.0, planted=False):
+    rng = np.random.default_rng(seed)
+    beams = rng.integers(0, V, size=(B, W, L)).astype(np.int32)
+    for b in range(B):
+        for i in range(1, W):
+            k = rng.integers(0, L)
+            beams[b, i, :k] = beams[b, 0, :k]
+    root = rng.integers(0, V, size=B).astype(np.int32)
+    T_cap = 1 + W * L
+    tr = oracle.build_tree_beams(beams, root, T_cap)
+    tgt = (3.0 * rng.standard_normal((B, T_cap, V))).astype(np.float32)
+    if planted:
+        for b in range(B):
+            i = rng.integers(0, W)
+            a = rng.integers(0, L + 1)
+            for k in range(a):
+                par = 0 if k == 0 else tr["beam_node"][b, i, k - 1]
+                tgt[b, par, beams[b, i, k]] = tgt[b, par].max() + 20.0
+    dft = (tgt + sigma * rng.standard_normal((B, T_cap, V))).astype(np.float32)
+    dft_row = np.tile(np.arange(T_cap, dtype=np.int32), (B, 1))
+    u_node = synth.exact_uniforms(rng, (B, T_cap))
+    u_final = synth.exact_uniforms(rng, (B,))
+    return dict(beams=beams, tr=tr, tgt=tgt, dft=dft, dft_row=dft_row, u_node=u_node,
+                u_final=u_final, W=W, L=L, B=B, V=V)
+
+
+def _run(oracle, mode, c):
+    tr = c["tr"]
+    return oracle.verify(mode, c["tgt"], None if mode == "greedy" else c["dft"],
+                         None if mode == "greedy" else c["dft_row"], tr["n_nodes"], tr["parent"],
+                         tr["token"], tr["depth"], c["u_node"], c["u_final"])
+
+
+def _inverse_cdf(w, u):
+    cdf = np.cumsum(w)
+    return int(min(np.searchsorted(cdf, u * cdf[-1], side="right"), len(w) - 1))
+
+
+# ----------------------------------------------------------------------------
+# GREEDY and REJECT_PATH against brute force over beams
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("W,L,V,planted", [(4, 4, 1000, True), (8, 5, 300, True),
+                                           (16, 4, 50, True), (3, 3, 7, False)])
+def test_greedy_is_brute_force_longest_prefix(oracle, W, L, V, planted):
+    c = _beam_case(oracle, 17 + W, 40, W, L, V, planted=planted)
+    res = _run(oracle, "greedy", c)
+    bn, beams, tgt = c["tr"]["beam_node"], c["beams"], c["tgt"]
+    lens = []
+    for b in range(c["B"]):
+        best_len, best_i = -1, -1
+        for i in range(W):
+            a = 0
+            for k in range(L):
+                par = 0 if k == 0 else bn[b, i, k - 1]
+                if beams[b, i, k] != int(np.argmax(tgt[b, par])):
+                    break
+                a += 1
+            if a > best_len:
+                best_len, best_i = a, i
+        stop = 0 if best_len == 0 else bn[b, best_i, best_len - 1]
+        assert res["acc_len"][b] == best_len
+        assert list(res["acc_path"][b, :best_len + 1]) == [0] + list(bn[b, best_i, :best_len])
+        assert np.all(res["acc_path"][b, best_len + 1:] == -1)
+        assert res["next_token"][b] == int(np.argmax(tgt[b, stop]))
+        lens.append(best_len)
+    if planted:
+        assert max(lens) >= 2          # the planted paths make the walk non-trivial
+
+
+@pytest.mark.parametrize("W,L,V,sigma", [(4, 4, 1000, 1.0), (8, 5, 64, 1.0), (16, 4, 40, 0.5)])
+def test_reject_path_is_per_beam_scan(oracle, W, L, V, sigma):
+    c = _beam_case(oracle, 5 + W, 60, W, L, V, sigma=sigma)
+    res = _run(oracle, "reject_path", c)
+    tr, bn, beams = c["tr"], c["tr"]["beam_node"], c["beams"]
+    checked = 0
+    for b in range(c["B"]):
+        if res["near_tie"][b]:
+            continue
+        T = tr["n_nodes"][b]
+        p = {t: softmax(c["tgt"][b, t].astype(np.float64)) for t in range(T)}
+        q = {t: softmax(c["dft"][b, t].astype(np.float64)) for t in range(T)}
+        best_len, best_i = -1, -1
+        for i in range(W):
+            a = 0
+            for k in range(L):
+                node = bn[b, i, k]
+                par = 0 if k == 0 else bn[b, i, k - 1]
+                x = beams[b, i, k]
+                ok = c["u_node"][b, node] < p[par][x] / q[par][x]
+                assert res["decision"][b, node] == int(ok)
+                np.testing.assert_allclose(res["p_tok"][b, node], p[par][x], rtol=1e-12)
+                np.testing.assert_allclose(res["q_tok"][b, node], q[par][x], rtol=1e-12)
+                if not ok:
+                    break
+                a += 1
+            if a > best_len:
+                best_len, best_i = a, i
+        stop = 0 if best_len == 0 else bn[b, best_i, best_len - 1]
+        assert res["acc_len"][b] == best_len
+        assert list(res["acc_path"][b, :best_len + 1]) == [0] + list(bn[b, best_i, :best_len])
+        has_child = np.any(tr["parent"][b, 1:T] == stop)
+        w = np.maximum(0.0, p[stop] - q[stop]) if has_child else p[stop]
+        assert res["next_token"][b] == _inverse_cdf(w, float(c["u_final"][b]))
+        checked += 1
+    assert checked >= c["B"] - 2
+
+
+# ----------------------------------------------------------------------------
+# residual chain: closed form, literal form, exact path marginal
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed,V,sigma", [(0, 16, 1.0), (1, 16, 1.5), (2, 50, 2.0), (3, 8, 0.3)])
+def test_closed_form_residual_equals_literal(oracle, seed, V, sigma):
+    rng = np.random.default_rng(seed)
+    lp = 3.0 * rng.standard_normal(V)
+    p = softmax(lp)
+    q = softmax(lp + sigma * rng.standard_normal(V))
+    K = 8
+    closed, Z, nc = oracle.residual_chain(p, q, K, literal=False)
+    lit, norms, nl = oracle.residual_chain(p, q, K, literal=True)
+    assert nc == nl
+    # Both forms divide a difference of O(1 + c_k) terms by Z_k, so fp64 rounding
+    # (eps = 2^-52) is amplified by (1 + c_k) / Z_k; V terms enter Z_k.
+    eps = np.finfo(np.float64).eps
+    c_k = np.concatenate([[0.0], np.cumsum(Z[:nc - 1])])
+    for k in range(nc):
+        tol = 1e-12 + 4 * V * eps * (1 + c_k[k]) / Z[k]
+        np.testing.assert_allclose(closed[k], lit[k], rtol=0, atol=tol)
+    # the literal normaliser of step k is the rejection probability Z_k / Z_{k-1}
+    for k in range(1, nc):
+        tol = 1e-12 + 4 * V * eps * (1 + c_k[k]) / Z[k]
+        np.testing.assert_allclose(norms[k], Z[k] / Z[k - 1], rtol=tol)
+
+
+@pytest.mark.parametrize("seed,V,N,sigma", [(0, 16, 1, 1.0), (1, 16, 4, 1.5), (2, 16, 8, 1.5),
+                                            (3, 40, 8, 3.0), (4, 5, 3, 0.1)])
+def test_exact_path_marginal_is_target(oracle, seed, V, N, sigma):
+    """ResiSpec page, Appendix B.1: accepted at candidate i, or all rejected."""
+    rng = np.random.default_rng(seed)
+    lp = 3.0 * rng.standard_normal(V)
+    p = softmax(lp)
+    q = softmax(lp + sigma * rng.standard_normal(V))
+    dist, Z, filled = oracle.residual_chain(p, q, N, literal=False)
+    marginal = np.zeros(V)
+    reach = 1.0                                   # probability that candidates 1..i-1 were rejected
+    for i in range(1, N + 1):
+        if i > filled:
+            break
+        cur = dist[i - 1]
+        marginal += reach * np.minimum(cur, q)     # x proposed by q and accepted
+        rho = 1.0 - np.minimum(cur, q).sum()       # rejection probability of candidate i
+        if i < filled:
+            np.testing.assert_allclose(rho, Z[i] / Z[i - 1], rtol=1e-9, atol=1e-15)
+        reach *= rho
+    if filled > N:
+        marginal += reach * dist[N]               # all rejected: draw from the final residual
+    np.testing.assert_allclose(marginal, p, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# chi-square over seeded trials
+# ----------------------------------------------------------------------------
+
+def _chi2_pvalue(counts, p):
+    n = counts.sum()
+    exp = n * p
+    order = np.argsort(exp)
+    c_s, e_s = counts[order].astype(np.float64), exp[order]
+    # merge the smallest bins until each merged bin expects at least 5
+    cb, eb, acc_c, acc_e = [], [], 0.0, 0.0
+    for cc, ee in zip(c_s, e_s):
+        acc_c += cc
+        acc_e += ee
+        if acc_e >= 5.0:
+            cb.append(acc_c)
+            eb.append(acc_e)
+            acc_c = acc_e = 0.0
+    if acc_e > 0:
+        cb[-1] += acc_c
+        eb[-1] += acc_e
+    cb, eb = np.array(cb), np.array(eb)
+    chi2 = ((cb - eb) ** 2 / eb).sum()
+    return stats.chi2.sf(chi2, len(cb) - 1)
+
+
+def _oracle_trials(oracle, mode, lp, lq, N, n_trials, seed, chunk=250_000):
+    """Root with N i.i.d. candidates from q; returns counts of the first emitted token
+    and the first-candidate acceptance count."""
+    V = len(lp)
+    q = softmax(lq.astype(np.float64))
+    rng = np.random.default_rng(seed)
+    counts = np.zeros(V, np.int64)
+    first_acc = 0
+    T_cap = N + 1
+    for start in range(0, n_trials, chunk):
+        B = min(chunk, n_trials - start)
+        cand = rng.choice(V, size=(B, N), p=q).astype(np.int32)
+        tr = oracle.build_tree_explicit(np.zeros((B, N), np.int32), cand,
+                                        np.zeros(B, np.int32), T_cap)
+        tgt = np.ascontiguousarray(np.broadcast_to(lp.astype(np.float32), (B, T_cap, V)))
+        dft = np.ascontiguousarray(np.broadcast_to(lq.astype(np.float32), (B, 1, V)))
+        dft_row = np.full((B, T_cap), -1, np.int32)
+        dft_row[:, 0] = 0
+        u_node = synth.exact_uniforms(rng, (B, T_cap))
+        u_final = synth.exact_uniforms(rng, (B,))
+        res = oracle.verify(mode, tgt, dft, dft_row, tr["n_nodes"], tr["parent"], tr["token"],
+                            tr["depth"], u_node, u_final)
+        first = res["acc_path"][:, 1]
+        x = np.where(res["acc_len"] >= 1, tr["token"][np.arange(B), np.maximum(first, 0)],
+                     res["next_token"])
+        counts += np.bincount(x, minlength=V)
+        first_acc += int((res["decision"][:, 1] == 1).sum())
+    return counts, first_acc
+
+
+def _logits(seed, V, sigma):
+    rng = np.random.default_rng(seed)
+    lp = (3.0 * rng.standard_normal(V)).astype(np.float32)
+    lq = (lp + sigma * rng.standard_normal(V)).astype(np.float32)
+    return lp, lq
+
+
+@pytest.mark.parametrize("N", [1, 2, 4, 8])
+def test_recursive_chi_square_1e6(oracle, N):
+    lp, lq = _logits(100 + N, 16, 1.5)
+    counts, first_acc = _oracle_trials(oracle, "reject_recursive", lp, lq, N, 1_000_000, seed=N)
+    p = softmax(lp.astype(np.float64))
+    q = softmax(lq.astype(np.float64))
+    assert _chi2_pvalue(counts, p) >= 1e-3
+    # first-candidate acceptance = sum min(p, q) = 1 - TV(p, q), within 4 sigma
+    alpha = np.minimum(p, q).sum()
+    n = 1_000_000
+    assert abs(first_acc / n - alpha) <= 4 * np.sqrt(alpha * (1 - alpha) / n)
+
+
+def test_reject_path_single_child_is_exact(oracle):
+    lp, lq = _logits(7, 16, 1.0)
+    counts, _ = _oracle_trials(oracle, "reject_path", lp, lq, 1, 1_000_000, seed=70)
+    assert _chi2_pvalue(counts, softmax(lp.astype(np.float64))) >= 1e-3
+
+
+@pytest.mark.parametrize("N", [2, 4])
+def test_negative_control_reject_path_siblings(oracle, N):
+    """Independent per-path tests over >= 2 i.i.d. siblings are not exact."""
+    lp, lq = _logits(200 + N, 16, 1.5)
+    counts, _ = _oracle_trials(oracle, "reject_path", lp, lq, N, 1_000_000, seed=N + 50)
+    assert _chi2_pvalue(counts, softmax(lp.astype(np.float64))) < 1e-3
+
+
+def _python_sequential(lp, lq, N, n, seed, variant):
+    """Vectorised sequential multi-candidate verification (third formulation) and mutants."""
+    p = softmax(lp.astype(np.float64))
+    q = softmax(lq.astype(np.float64))
+    V = len(p)
+    rng = np.random.default_rng(seed)
+    cand = rng.choice(V, size=(n, N), p=q)
+    u = rng.random((n, N))
+    uf = rng.random(n)
+    cur = np.tile(p, (n, 1))
+    out = np.full(n, -1)
+    active = np.ones(n, bool)
+    rows = np.arange(n)
+    for i in range(N):
+        x = cand[:, i]
+        ratio = cur[rows, x] / q[x]
+        acc = active & (u[:, i] < ratio)
+        out[acc] = x[acc]
+        active &= ~acc
+        res = np.maximum(0.0, cur - q[None, :])
+        if variant != "no_renorm":
+            s = res.sum(1, keepdims=True)
+            res = np.divide(res, s, out=np.zeros_like(res), where=s > 0)
+        cur = np.where(active[:, None], res, cur)
+    final = np.tile(p, (n, 1)) if variant == "resample_from_p" else cur
+    cdf = np.cumsum(final, axis=1)
+    pick = (cdf <= (uf * cdf[:, -1])[:, None]).sum(1)
+    pick = np.minimum(pick, V - 1)
+    out[active] = pick[active]
+    return np.bincount(out, minlength=V), p
+
+
+def test_python_formulation_passes_and_mutants_fail():
+    lp, lq = _logits(300, 16, 1.5)
+    counts, p = _python_sequential(lp, lq, 4, 1_000_000, 1, "correct")
+    assert _chi2_pvalue(counts, p) >= 1e-3
+    for variant in ("resample_from_p", "no_renorm"):
+        counts, p = _python_sequential(lp, lq, 4, 1_000_000, 2, variant)
+        assert _chi2_pvalue(counts, p) < 1e-3, variant
+
+
+# ----------------------------------------------------------------------------
+# special cases
+# ----------------------------------------------------------------------------
+
+def test_q_equal_p_accepts_first_candidate(oracle):
+    lp, _ = _logits(9, 32, 1.0)
+    B, N, V = 500, 4, 32
+    rng = np.random.default_rng(9)
+    cand = rng.integers(0, V, size=(B, N)).astype(np.int32)
+    tr = oracle.build_tree_explicit(np.zeros((B, N), np.int32), cand, np.zeros(B, np.int32), N + 1)
+    tgt = np.ascontiguousarray(np.broadcast_to(lp, (B, N + 1, V)))
+    dft = np.ascontiguousarray(np.broadcast_to(lp, (B, 1, V)))
+    dft_row = np.full((B, N + 1), -1, np.int32)
+    dft_row[:, 0] = 0
+    for mode in ("reject_path", "reject_recursive"):
+        res = oracle.verify(mode, tgt, dft, dft_row, tr["n_nodes"], tr["parent"], tr["token"],
+                            tr["depth"], synth.exact_uniforms(rng, (B, N + 1)),
+                            synth.exact_uniforms(rng, (B,)))
+        assert np.all(res["decision"][:, 1] == 1)
+        assert np.all(res["acc_len"] == 1)
+
+
+def test_one_hot_target_follows_greedy_path(oracle):
+    c = _beam_case(oracle, 31, 50, 6, 4, 12, planted=True)
+    # make every target row one-hot in fp64: the row maximum gets +1000
+    tgt = c["tgt"]
+    B, T_cap, V = tgt.shape
+    idx = tgt.argmax(axis=2)
+    for b in range(B):
+        for t in range(T_cap):
+            tgt[b, t, idx[b, t]] += 1000.0
+    greedy = _run(oracle, "greedy", c)
+    rec = _run(oracle, "reject_recursive", c)
+    assert np.array_equal(greedy["acc_len"], rec["acc_len"])
+    assert np.array_equal(greedy["acc_path"], rec["acc_path"])
+    assert np.array_equal(greedy["next_token"], rec["next_token"])
+    visited = rec["decision"] >= 0
+    assert np.array_equal(rec["decision"][visited], greedy["decision"][visited])
+
+
+def test_workload_inputs_run_through_oracle(oracle):
+    """Workload 0 in both of its modes, end to end through the oracle."""
+    inp = synth.make_inputs(0)
+    tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+    for mode in inp["modes"]:
+        res = oracle.verify(mode, inp["tgt"], inp["dft"] if mode != "greedy" else None,
+                            inp["dft_row"] if mode != "greedy" else None, tr["n_nodes"],
+                            tr["parent"], tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
+        assert 0 <= res["acc_len"][0] <= 4
+        assert 0 <= res["next_token"][0] < inp["V"]
