@@ -1,0 +1,250 @@
+"""Benchmark of one speculative verification step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic input: spec_build_tree,
+spec_tree_attention, spec_verify and spec_kv_compact, enqueued on one stream,
+preceded by restoring the sequence's context length (the commit advances it).
+Inputs already sit in HBM.  To keep the measurement honest about HBM (the
+256 MB Infinity Cache would otherwise hold a small workload), the timed steps
+rotate over several independent input sets whose total exceeds twice the
+cache, so each step reads data that was evicted since its last use.
+
+Prints one JSON line: verified tree tokens/s (draft nodes checked per second),
+the roofline of the dominant kernel measured with HIP events on the launch
+stream, and the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+import numpy as np
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+METRIC = "verified tree tokens/s per verify step; attention+verify HBM GB/s as % of peak"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive")
+    ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def attention_bytes(inp, n_nodes):
+    """Algorithmic HBM bytes of one spec_tree_attention launch.
+
+    Per sequence: K and V of every context slot and tree slot of every KV head,
+    the tree's queries and outputs, and the ancestor masks.
+    """
+    esz = 4 if inp["dtype"] == "f32" else 2
+    D, H, Hkv = inp["D"], inp["H"], inp["Hkv"]
+    n_words = (inp["T_cap"] + 63) // 64
+    total = 0
+    for b in range(inp["B"]):
+        T = int(n_nodes[b])
+        keys = int(inp["ctx_len"][b]) + T
+        total += 2 * Hkv * keys * D * esz          # K and V
+        total += 2 * T * H * D * esz               # q in, out
+        total += T * n_words * 8                   # masks
+    return total
+
+
+def verify_bytes(inp, n_nodes, parent, dft_row, mode):
+    """Algorithmic HBM bytes of one spec_verify launch (one pass over every needed row).
+
+    Every target row of the tree (any node can be the stop node) and, in the
+    rejection modes, every draft row of a node with children.
+    """
+    V = inp["V"]
+    total = 0
+    for b in range(inp["B"]):
+        T = int(n_nodes[b])
+        total += T * V * 4
+        if mode != "greedy":
+            has_child = set(int(p) for p in parent[b, 1:T])
+            rows = {int(dft_row[b, t]) for t in has_child}
+            total += len(rows) * V * 4
+    return total
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    import __graft_entry__  # noqa: F401  (puts the repo on sys.path)
+    from tree_attention_verification_beam_amd import binding as sv
+    from tree_attention_verification_beam_amd import pipeline, synth
+
+    sv.load()
+    wl = synth.WORKLOADS[args.workload]
+    mode = args.mode or wl.modes[0]
+    dev = torch.device("cuda:0")
+
+    # ---------------------------------------------------------------- input sets
+    first = synth.make_inputs(args.workload, 0)
+    set_bytes = first["k"].nbytes + first["v"].nbytes + first["tgt"].nbytes
+    if mode != "greedy" and first["dft"] is not None:
+        set_bytes += first["dft"].nbytes
+    n_sets = args.sets or max(1, min(32, -(-2 * MALL_BYTES // set_bytes)))
+    steps_all = []
+    for s in range(n_sets):
+        inp = first if s == 0 else synth.make_inputs(args.workload, s)
+        steps_all.append((inp, pipeline.Step(inp, mode, device=dev)))
+        print(f"[bench] set {s + 1}/{n_sets} ready", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(i):
+        inp, st = steps_all[i % n_sets]
+        st.ctx_len.copy_(st.ctx0, non_blocking=True)
+        st.launch(compact=True)
+
+    # tree sizes (outside any timed region)
+    for i in range(n_sets):
+        steps_all[i][1].build_tree()
+    torch.cuda.synchronize()
+    n_draft = [int(st.n_nodes.sum().item()) - st.B for _, st in steps_all]
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    # ---------------------------------------------------------------- timed steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        inp, st = steps_all[i % n_sets]
+        st.ctx_len.copy_(st.ctx0, non_blocking=True)
+        st.build_tree()
+        ev[i][0].record(stream)
+        st.attention()
+        ev[i][1].record(stream)
+        st.verify()
+        st.compact()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    verified = sum(n_draft[i % n_sets] for i in range(args.steps))
+    value = verified / (t1 - t0)
+    attn_ms = [a.elapsed_time(b) for a, b in ev]
+    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
+
+    # ---------------------------------------------------------------- per-call breakdown
+    names = ("build", "attention", "verify", "compact")
+    evs = {n: [] for n in names}
+    for i in range(min(args.steps, 4 * n_sets)):
+        inp, st = steps_all[i % n_sets]
+        st.ctx_len.copy_(st.ctx0, non_blocking=True)
+        for n, fn in zip(names, (st.build_tree, st.attention, st.verify, st.compact)):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs[n].append((a, b))
+    torch.cuda.synchronize()
+    brk = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) * 1e3 for n in names}
+
+    # algorithmic bytes (averaged over the rotation)
+    a_bytes, v_bytes = [], []
+    for inp, st in steps_all:
+        nn = st.n_nodes.cpu().numpy()
+        a_bytes.append(attention_bytes(inp, nn))
+        v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
+                                    inp["dft_row"] if inp["dft_row"] is not None else None, mode))
+    a_avg = float(np.mean([a_bytes[i % n_sets] for i in range(args.steps)]))
+    v_avg = float(np.mean(v_bytes))
+    achieved = a_avg / attn_avg_s / 1e9
+    status = max(int(st.status.item()) for _, st in steps_all)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "verified tree tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "ctx": wl.ctx, "H": wl.H, "Hkv": wl.Hkv,
+                   "D": wl.D, "V": wl.V, "tree": wl.tree, "mode": mode, "T_cap": wl.T_cap,
+                   "draft_nodes_per_step": float(np.mean(n_draft)), "input_sets": n_sets},
+        "roofline": {"bound": "hbm", "kernel": "spec_tree_attention", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": None, "algorithmic_bytes_per_launch": a_avg,
+                     "avg_launch_us": attn_avg_s * 1e6},
+        "breakdown_us": brk,
+        "attention_verify": {
+            "attention_GBps": a_avg / (brk["attention"] * 1e-6) / 1e9,
+            "verify_GBps": v_avg / (brk["verify"] * 1e-6) / 1e9,
+            "verify_bytes_per_launch": v_avg,
+            "attention_plus_verify_frac_of_peak":
+                (a_avg + v_avg) / ((brk["attention"] + brk["verify"]) * 1e-6) / 1e9
+                / HBM_PEAK_GBPS,
+        },
+        "device_status": status,
+    }
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(first, mode, args.cpu_sample_s)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(inp, mode, budget_s):
+    """The oracle as it stands, single-threaded, on full steps of the same workload."""
+    import oracle
+    oracle.build()
+    done, draft, t_total = 0, 0, 0.0
+    while t_total < budget_s and done < 50:
+        t0 = time.perf_counter()
+        if inp["tree"] == "beams":
+            tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+        else:
+            tr = oracle.build_tree_explicit(inp["cand_parent"], inp["cand_token"],
+                                            inp["root_token"], inp["T_cap"])
+        oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                              tr["anc"])
+        g = mode == "greedy"
+        res = oracle.verify(mode, inp["tgt"], None if g else inp["dft"],
+                            None if g else inp["dft_row"], tr["n_nodes"], tr["parent"],
+                            tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
+        k, v = inp["k"].copy(), inp["v"].copy()
+        oracle.kv_compact(k, v, inp["ctx_len"], res["acc_len"], res["acc_path"])
+        t_total += time.perf_counter() - t0
+        done += 1
+        draft += int(tr["n_nodes"].sum()) - inp["B"]
+        if t_total > 0.5 * budget_s:
+            break
+    return {"value": draft / t_total, "unit": "verified tree tokens/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{done} full step(s) of workload {inp['name']} (build, attention over all "
+                      f"rows, {mode} verify, compact), fp64 single-threaded C; "
+                      f"{t_total:.1f} s on {os.cpu_count()} visible host cores"}
+
+
+if __name__ == "__main__":
+    main()

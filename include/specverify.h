@@ -1,0 +1,225 @@
+/*
+ * specverify.h -- C ABI of the speculative-verification library for AMD MI355X
+ * (gfx950): token-tree build, tree-masked GQA attention, acceptance/selection
+ * with residual resampling, and the KV commit of the accepted path.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [ReDrafter] "Recurrent Drafter for Fast Speculative Decoding in Large
+ *               Language Models", sections "Dynamic Tree Attention" and "The
+ *               Full Speculative Decoding Loop" (Steps 3-6).
+ *   [Clover]    "Clover: Regressive Lightweight Speculative Decoding with
+ *               Sequential Knowledge", section "Inference-Time Verification:
+ *               Token Tree Construction and Tree Attention" (Figure 4 mask).
+ *   [ResiSpec]  paperpeel 2608.24411 (residual drift in multi-candidate
+ *               speculative decoding), section 4 (residual distribution and
+ *               sequential verification of N candidates).
+ *
+ * General contract
+ *   - Every pointer argument is caller-owned DEVICE memory unless stated
+ *     otherwise.  The library never allocates; scratch memory ("workspace") is
+ *     passed in, sized by the matching *_workspace_size query, 256-byte aligned.
+ *   - Every call validates its host-side arguments, returns a negative
+ *     spec_status without launching anything on a violation, and otherwise
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = default stream)
+ *     and returns SPEC_OK without synchronising.
+ *   - Problems only visible on the device (a bad parent index, a token outside
+ *     the vocabulary, a context that overflows the cache) are OR-ed into the
+ *     optional device status word `status` (int32, SPEC_DEV_* bits); the
+ *     affected sequence gets a defined, safe result (see each call).  The word
+ *     is never cleared by the library.
+ *   - Results are bitwise deterministic from run to run.
+ *
+ * Tree conventions
+ *   - Tree position 0 is the root: the last token the target produced, whose
+ *     K/V are not in the context yet.  Draft nodes are 1..T_b-1, where
+ *     T_b = n_nodes[b] counts the root ([Clover] counts tree size without the
+ *     root; T_b = size + 1).  T_cap >= every T_b bounds all per-node arrays;
+ *     T_cap <= SPEC_MAX_TREE.
+ *   - Every parent index is smaller than its child's.
+ *   - anc[b][t] is a bitmask of ceil(T_cap/64) uint64 words: bit a (word a/64,
+ *     bit a%64) is set iff node a is t itself, the root or an ancestor of t
+ *     ([Clover] Figure 4: M_ij = 1 iff j is an ancestor of i or i = j).
+ *   - Padding nodes t >= T_b have parent = token = depth = -1 and anc = 0.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_MAX_TREE 128 /* largest T_cap (root included) */
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_ERR_INVALID = -1,     /* bad argument value or null pointer            */
+    SPEC_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head dim)     */
+    SPEC_ERR_CAPACITY = -3,    /* a size exceeds a capacity (T_cap, cache cap)  */
+    SPEC_ERR_WORKSPACE = -4,   /* workspace missing, too small or misaligned    */
+    SPEC_ERR_HIP = -5          /* the HIP runtime refused a launch              */
+} spec_status;
+
+/* device status bits (OR-ed into *status) */
+#define SPEC_DEV_BAD_PARENT 0x1   /* explicit tree not topological               */
+#define SPEC_DEV_BAD_TOKEN 0x2    /* token outside [0, V)                        */
+#define SPEC_DEV_BAD_ROW 0x4      /* an inner node has no valid draft row        */
+#define SPEC_DEV_CTX_RANGE 0x8    /* ctx_len + n_nodes > cache capacity, etc.    */
+#define SPEC_DEV_RESIDUAL_ZERO 0x10 /* a residual had no mass (rounding only)    */
+#define SPEC_DEV_SYNC_TIMEOUT 0x20  /* a cross-workgroup wait gave up            */
+#define SPEC_DEV_BAD_TREE 0x40    /* n_nodes/parent/depth inconsistent           */
+
+typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
+typedef enum { SPEC_TREE_BEAMS = 0, SPEC_TREE_EXPLICIT = 1 } spec_tree_kind;
+typedef enum {
+    SPEC_GREEDY = 0,
+    SPEC_REJECT_PATH = 1,
+    SPEC_REJECT_RECURSIVE = 2
+} spec_verify_mode;
+
+/* Library version as 10000*major + 100*minor + patch (host only). */
+int spec_version(void);
+
+/* Name of a spec_status value (static string, host only). */
+const char *spec_status_string(int status);
+
+/*
+ * spec_build_tree -- pack draft candidates into a token tree.
+ *
+ * [ReDrafter] "Dynamic Tree Attention": beam-search candidates of equal length
+ * share prefixes; the packed beam keeps every distinct prefix once and the tree
+ * mask lets each token attend only to its own prefix.  Static trees of parallel
+ * heads ([Clover] "Token tree construction") and i.i.d. multi-candidate trees
+ * ([ResiSpec] section 4) come in explicit form.
+ *
+ * kind == SPEC_TREE_BEAMS:
+ *   cand_token [B][W][L] int32: W candidates of L tokens each (the root is not
+ *   part of them); cand_parent must be NULL.  Nodes are numbered in beam-major
+ *   order of first appearance of each distinct prefix.  Requires
+ *   1 + W*L <= T_cap.  beam_node [B][W][L] (nullable) receives the node holding
+ *   each candidate's prefix of length k+1.
+ * kind == SPEC_TREE_EXPLICIT:
+ *   N = W*L candidates (pass W = 1, L = N); cand_token [B][N] and
+ *   cand_parent [B][N] int32 give node j+1's token and its parent's tree index,
+ *   which must lie in [0, j].  Duplicate siblings are kept.  A sequence whose
+ *   parent list is not topological becomes a root-only tree and raises
+ *   SPEC_DEV_BAD_PARENT.  beam_node must be NULL.  Requires 1 + N <= T_cap.
+ * root_token [B]: token of node 0.
+ * Outputs: n_nodes [B] (T_b, root included), parent/token/depth [B][T_cap],
+ * anc [B][T_cap][ceil(T_cap/64)] uint64.
+ */
+int spec_build_tree(int kind, int B, int W, int L, int T_cap, const int32_t *cand_token,
+                    const int32_t *cand_parent, const int32_t *root_token, int32_t *n_nodes,
+                    int32_t *parent, int32_t *token, int32_t *depth, uint64_t *anc,
+                    int32_t *beam_node, int32_t *status, void *stream);
+
+/*
+ * spec_tree_attention -- one attention pass of every tree query over the
+ * context plus its own tree prefix.
+ *
+ * [ReDrafter] Step 4: the target processes the packed beam in one forward pass
+ * under the tree mask, and each token's result equals the one it would get had
+ * its prefix been decoded token by token.  For sequence b, node t < T_b and
+ * query head h (KV head g = h / (H/Hkv); consecutive query heads share a KV
+ * head): keys are the context slots 0..ctx-1 and the tree slots ctx+a for every
+ * a with anc bit a set; out = softmax(scale * q.k) v over those keys.
+ *
+ * dt: SPEC_F32 (q, caches and out fp32) or SPEC_BF16 (bf16; fp32 accumulation
+ * and softmax).  D must be 64 or 128 for bf16, 1..256 for fp32.
+ * q [B][T_cap][H][D]; k_cache, v_cache [B][Hkv][cache_cap][D]: the tree's own
+ * K/V already sit at slots ctx..ctx+T_b-1 (node t at ctx+t); ctx_len [B]
+ * (device) with ctx_len[b] <= max_ctx (host bound used to size the launch);
+ * n_nodes [B]; anc as above.  scale <= 0 selects 1/sqrt(D).
+ * out [B][T_cap][H][D] (same dtype as q): rows t >= T_b are zero.  A sequence
+ * with ctx_len[b] + n_nodes[b] > cache_cap or ctx_len[b] > max_ctx gets zero
+ * rows and raises SPEC_DEV_CTX_RANGE.
+ * ws: spec_tree_attention_workspace_size() bytes (may be 0 bytes / NULL when
+ * the query returns 0).
+ */
+size_t spec_tree_attention_workspace_size(int dt, int B, int T_cap, int H, int Hkv, int D,
+                                          int max_ctx);
+int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cache_cap,
+                        int max_ctx, const void *q, const void *k_cache, const void *v_cache,
+                        const int32_t *ctx_len, const int32_t *n_nodes, const uint64_t *anc,
+                        float scale, void *out, void *ws, size_t ws_bytes, int32_t *status,
+                        void *stream);
+
+/*
+ * spec_verify -- accept a prefix of the tree per sequence and draw the next token.
+ *
+ * p_t = softmax(tgt[b][t]) is the target distribution after node t;
+ * q_t = softmax(dft[b][dft_row[b][t]]) the draft distribution the children of
+ * t were drawn from.  Node t >= 1 with parent s and token x is tested:
+ *   SPEC_GREEDY           ([ReDrafter] Step 5, token matches): accepted iff
+ *                         x == argmax p_s (lowest index on ties).
+ *   SPEC_REJECT_PATH      ([ReDrafter] Step 5, rejection sampling): accepted iff
+ *                         u_node[t] < p_s(x) / q_s(x), independently per node.
+ *   In both, a node survives when it and all its ancestors are accepted; the
+ *   deepest survivor wins, lowest node index on ties (= lowest beam index).  The
+ *   next token at the stop node s is argmax p_s (GREEDY), or is drawn with
+ *   u_final from norm(max(0, p_s - q_s)) if s has children and from p_s if it
+ *   is a leaf (REJECT_PATH).
+ *   SPEC_REJECT_RECURSIVE ([ResiSpec] section 4): from the root, the children of
+ *                         the current node s are tested in index order against
+ *                         a running target p' (p_s at first): accept x iff
+ *                         u_node[child] < p'(x) / q_s(x); each rejection sets
+ *                         p' <- norm(max(0, p' - q_s)).  An acceptance moves to
+ *                         that child.  With no child left, the next token is
+ *                         drawn from p' with u_final.
+ * Draws are inverse-CDF in ascending vocabulary order: the smallest v whose
+ * running sum exceeds u_final * total.
+ *
+ * tgt [B][T_cap][V] fp32; dft [B][R][V] fp32 and dft_row [B][T_cap] (entries
+ * in [0, R) for every node with children; -1 otherwise) -- both NULL (R = 0)
+ * in SPEC_GREEDY; n_nodes/parent/token/depth from spec_build_tree; u_node
+ * [B][T_cap] and u_final [B] in [0, 1) (u_node[b][0] unused).
+ * Outputs: acc_len [B] (depth of the stop node); acc_path [B][T_cap] (node ids
+ * root first, -1 after the path); next_token [B]; p_tok, q_tok [B][T_cap]
+ * (nullable: p_s(x) and q_s(x) of each node's own token under its parent; 0
+ * for the root, for padding and q in GREEDY); decision [B][T_cap] int8
+ * (nullable: 1 accepted, 0 rejected, -1 untested); near_tie [B] (nullable:
+ * count of decisions with |ratio - u| < 1e-5 plus one if the draw's threshold
+ * fell within 1e-9 of a running-sum boundary).
+ * A bad token or missing draft row raises a SPEC_DEV_* bit and the sequence
+ * accepts nothing (acc_len 0, next_token = argmax p_0).
+ * ws: spec_verify_workspace_size() bytes.
+ */
+size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R);
+int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, const float *dft,
+                const int32_t *dft_row, const int32_t *n_nodes, const int32_t *parent,
+                const int32_t *token, const int32_t *depth, const float *u_node,
+                const float *u_final, int32_t *acc_len, int32_t *acc_path, int32_t *next_token,
+                float *p_tok, float *q_tok, int8_t *decision, int32_t *near_tie, void *ws,
+                size_t ws_bytes, int32_t *status, void *stream);
+
+/*
+ * spec_kv_compact -- commit the accepted path's K/V to contiguous cache slots.
+ *
+ * [ReDrafter] Step 6: the accepted tokens join the context and the next step
+ * starts from the last accepted position.  For every b and i = 1..acc_len[b]:
+ * slot ctx + acc_path[b][i] moves to slot ctx + i, for K and V of all Hkv heads
+ * (all sources are read before any slot is written, so overlapping moves are
+ * safe); the root stays at slot ctx.  Then ctx_len[b] += acc_len[b] + 1 (the
+ * root and the accepted tokens; next_token is the next step's root).
+ * dt selects the element size; k_cache, v_cache [B][Hkv][cache_cap][D] in
+ * place; ctx_len [B] in/out; acc_len [B], acc_path [B][T_cap] from spec_verify.
+ * A path that is not increasing or leaves the cache raises SPEC_DEV_CTX_RANGE
+ * and that sequence is left untouched.
+ */
+int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int T_cap, void *k_cache,
+                    void *v_cache, int32_t *ctx_len, const int32_t *acc_len,
+                    const int32_t *acc_path, int32_t *status, void *stream);
+
+/*
+ * spec_copy_probe -- plain streaming copy of n_bytes (multiple of 16) from src
+ * to dst, for bandwidth and memory-counter calibration of the platform.
+ */
+int spec_copy_probe(const void *src, void *dst, size_t n_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

@@ -1,0 +1,66 @@
+"""The C-ABI library loads and exports every entry point include/specverify.h
+declares, with the binding's argument counts matching the header.  Host-only
+calls (version, status strings, workspace queries, argument validation that
+returns before any launch) run without a GPU."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "specverify.h"
+
+
+def declared():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(?:int|size_t|const char\s*\*)\s*(spec_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [p for p in m.group(2).split(",") if p.strip() and p.strip() != "void"]
+        out[m.group(1)] = len(params)
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from tree_attention_verification_beam_amd import binding
+    if not binding.LIB_PATH.exists():
+        import __graft_entry__
+        __graft_entry__.build()
+    return binding
+
+
+def test_header_lists_the_four_calls():
+    d = declared()
+    for name in ("spec_build_tree", "spec_tree_attention", "spec_verify", "spec_kv_compact"):
+        assert name in d
+
+
+def test_every_declared_symbol_is_exported_and_bound(lib):
+    cdll = lib.load()
+    for name, n_args in declared().items():
+        assert hasattr(cdll, name), name
+        assert name in lib.SIGNATURES, name
+        assert len(lib.SIGNATURES[name][1]) == n_args, name
+
+
+def test_host_only_calls(lib):
+    cdll = lib.load()
+    assert cdll.spec_version() >= 100
+    assert cdll.spec_status_string(-3) == b"SPEC_ERR_CAPACITY"
+    # workspace queries are pure host arithmetic
+    assert cdll.spec_verify_workspace_size(0, 64, 17, 128000, 0) > 0
+    assert cdll.spec_tree_attention_workspace_size(1, 64, 17, 32, 32, 128, 1024) == 0
+    assert cdll.spec_tree_attention_workspace_size(1, 4, 49, 32, 8, 128, 32768) > 0
+
+
+def test_validation_rejects_before_launch(lib):
+    cdll = lib.load()
+    # T_cap above the limit, bad mode, bad head grouping: rejected on the host
+    assert cdll.spec_build_tree(0, 1, 4, 4, 129, 1, None, 1, 1, 1, 1, 1, 1, None, None, None) == -3
+    assert cdll.spec_build_tree(0, 1, 8, 8, 17, 1, None, 1, 1, 1, 1, 1, 1, None, None, None) == -3
+    assert cdll.spec_verify(7, 1, 17, 100, 0, *([1] * 17), 0, None, None) == -1
+    assert cdll.spec_tree_attention(1, 1, 17, 6, 4, 128, 100, 64, *([1] * 6), 0.0, 1, None, 0,
+                                    None, None) == -1
+    assert cdll.spec_kv_compact(1, 1, 8, 128, 10, 200, *([1] * 5), None, None) == -3

@@ -1,0 +1,218 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: tree outputs, index outputs and accept decisions bit-exact (sequences
+with a near-tie on either side are excluded and counted); attention within
+max|diff| <= 1e-2 * max|ref| (bf16 inputs, fp32 accumulation; fp32 path the
+same bar); p/q of the drafted tokens within 1e-5 absolute.
+
+Oracle-sized cases keep every workload's shapes and structure but shrink B or
+ctx so the fp64 oracle finishes in seconds while still spanning several key
+tiles and a ragged tail; the full-size workloads are compared on every verify
+output and on sampled attention rows.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_attention_verification_beam_amd import pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    0: dict(),
+    1: dict(),
+    2: dict(B_override=4),
+    3: dict(B_override=2, ctx_override=1000),
+    4: dict(B_override=1, ctx_override=3000),
+}
+EXTRA_MODES = {0: ("reject_recursive",), 1: ("reject_recursive",)}
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_tree(inp):
+    if inp["tree"] == "beams":
+        return oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+    return oracle.build_tree_explicit(inp["cand_parent"], inp["cand_token"], inp["root_token"],
+                                      inp["T_cap"])
+
+
+def oracle_verify(inp, tr, mode, tgt=None):
+    tgt = inp["tgt"] if tgt is None else tgt
+    g = mode == "greedy"
+    return oracle.verify(mode, tgt, None if g else inp["dft"], None if g else inp["dft_row"],
+                         tr["n_nodes"], tr["parent"], tr["token"], tr["depth"], inp["u_node"],
+                         inp["u_final"])
+
+
+def plant_greedy(inp, tr, seed):
+    """Raise the target logit of a random beam prefix so greedy acceptance is non-trivial."""
+    tgt = inp["tgt"].copy()
+    rng = np.random.default_rng(seed)
+    B = inp["B"]
+    for b in range(B):
+        if inp["tree"] == "beams":
+            i = rng.integers(0, inp["W"])
+            a = rng.integers(1, inp["L"] + 1)
+            for k in range(a):
+                par = 0 if k == 0 else tr["beam_node"][b, i, k - 1]
+                tgt[b, par, inp["beams"][b, i, k]] = tgt[b, par].max() + 20.0
+    return tgt
+
+
+def assert_tree_equal(res, tr):
+    for key in ("n_nodes", "parent", "token", "depth", "anc"):
+        assert np.array_equal(res[key], tr[key]), key
+    if "beam_node" in res:
+        assert np.array_equal(res["beam_node"], tr["beam_node"])
+
+
+def assert_verify_equal(res, ref, what):
+    B = len(ref["acc_len"])
+    ties = (res["near_tie"] > 0) | (ref["near_tie"] > 0)
+    ok = ~ties
+    for key in ("acc_len", "acc_path", "next_token", "decision"):
+        a, b = res[key][ok], ref[key][ok]
+        if not np.array_equal(a, b):
+            bad = np.flatnonzero(~np.all((res[key] == ref[key]).reshape(B, -1), axis=1) & ok)
+            raise AssertionError(f"{what}: {key} differs for sequences {bad[:8]}: "
+                                 f"gpu {res[key][bad[:2]]} oracle {ref[key][bad[:2]]}")
+    dp = np.abs(res["p_tok"] - ref["p_tok"]).max()
+    dq = np.abs(res["q_tok"] - ref["q_tok"]).max()
+    assert dp <= 1e-5 and dq <= 1e-5, (what, dp, dq)
+    assert ties.sum() <= max(1, B // 10), (what, "near-ties", int(ties.sum()))
+    log(f"  {what}: B={B} near-tie sequences={int(ties.sum())} max|dp|={dp:.2e} "
+        f"max|dq|={dq:.2e} acc_len mean={res['acc_len'].mean():.2f}")
+
+
+def attn_bar(gpu_rows, ref_rows, what):
+    err = np.abs(gpu_rows.astype(np.float64) - ref_rows).max()
+    bound = 1e-2 * np.abs(ref_rows).max()
+    log(f"  {what}: attention max|diff|={err:.3e} bound={bound:.3e}")
+    assert err <= bound, (what, err, bound)
+
+
+# --------------------------------------------------------------------------- reduced cases
+
+@pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("seed", [100, 200])
+def test_reduced_workload(gpu, wid, seed):
+    inp = synth.make_inputs(wid, seed, **REDUCED[wid])
+    log(f"case reduced wid={wid} seed={seed} B={inp['B']} ctx={inp['ctx']}")
+    tr = oracle_tree(inp)
+    modes = tuple(inp["modes"]) + EXTRA_MODES.get(wid, ())
+    for mode in modes:
+        step = pipeline.Step(inp, mode)
+        res = step.run(compact=False)
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_tree_equal(res, tr)
+        assert_verify_equal(res, oracle_verify(inp, tr, mode), f"wid={wid} {mode}")
+        if mode == modes[0]:
+            ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"],
+                                        tr["n_nodes"], tr["anc"])
+            attn_bar(res["attn"], ref, f"wid={wid}")
+            # KV commit, bitwise against the oracle on host copies
+            k0, v0 = inp["k"].copy(), inp["v"].copy()
+            step.compact()
+            torch.cuda.synchronize()
+            new_ctx = oracle.kv_compact(k0, v0, inp["ctx_len"], res["acc_len"], res["acc_path"])
+            kk = step.k.view(torch.int16 if step.k.dtype == torch.bfloat16 else torch.int32)
+            vv = step.v.view(torch.int16 if step.v.dtype == torch.bfloat16 else torch.int32)
+            assert np.array_equal(kk.cpu().numpy().view(k0.dtype), k0)
+            assert np.array_equal(vv.cpu().numpy().view(v0.dtype), v0)
+            assert np.array_equal(step.ctx_len.cpu().numpy(), new_ctx)
+            assert int(step.status.item()) == 0
+    if inp["tree"] == "beams":
+        tgt = plant_greedy(inp, tr, seed)
+        inp2 = dict(inp, tgt=tgt)
+        step = pipeline.Step(inp2, "greedy", with_kv=False)
+        res = step.run()
+        ref = oracle_verify(inp2, tr, "greedy")
+        assert_verify_equal(res, ref, f"wid={wid} greedy planted")
+        assert ref["acc_len"].max() >= 1
+
+
+# --------------------------------------------------------------------------- full size
+
+@pytest.fixture(scope="module", params=[1, 2, 3, 4])
+def full(request):
+    wid = request.param
+    log(f"case full wid={wid}: generating inputs")
+    inp = synth.make_inputs(wid, 0)
+    return wid, inp, oracle_tree(inp)
+
+
+def test_full_size(gpu, full):
+    wid, inp, tr = full
+    mode = inp["modes"][0]
+    log(f"case full wid={wid} mode={mode}")
+    step = pipeline.Step(inp, mode)
+    res = step.run(compact=False)
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    assert_tree_equal(res, tr)
+    assert_verify_equal(res, oracle_verify(inp, tr, mode), f"full wid={wid} {mode}")
+    # sampled attention rows: the last tree rows of every sequence plus random rows
+    rng = np.random.default_rng(wid)
+    B, T_cap, H = inp["B"], inp["T_cap"], inp["H"]
+    rows = []
+    for b in range(B):
+        T = tr["n_nodes"][b]
+        for t in (0, T - 1, rng.integers(0, T)):
+            rows.append((b, int(t), int(rng.integers(0, H))))
+    for _ in range(96):
+        b = int(rng.integers(0, B))
+        rows.append((b, int(rng.integers(0, tr["n_nodes"][b])), int(rng.integers(0, H))))
+    rows = np.array(rows, np.int32)
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"], rows=rows)
+    got = res["attn"][rows[:, 0], rows[:, 1], rows[:, 2]]
+    attn_bar(got, ref, f"full wid={wid} ({len(rows)} sampled rows)")
+    # padding rows are zero at any size
+    for b in range(B):
+        assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)
+    # KV commit: moved slots equal the pre-commit slots of the path, others untouched
+    k_before = step.k.clone()
+    step.compact()
+    torch.cuda.synchronize()
+    ctx = inp["ctx_len"]
+    for b in range(B):
+        n = int(res["acc_len"][b])
+        src = torch.tensor([ctx[b] + res["acc_path"][b, i] for i in range(1, n + 1)],
+                           dtype=torch.long, device=step.k.device)
+        if n:
+            assert torch.equal(step.k[b][:, ctx[b] + 1:ctx[b] + n + 1], k_before[b][:, src])
+        assert torch.equal(step.k[b][:, :ctx[b] + 1], k_before[b][:, :ctx[b] + 1])
+    assert np.array_equal(step.ctx_len.cpu().numpy(), ctx + res["acc_len"] + 1)
+    assert int(step.status.item()) == 0
+
+
+# --------------------------------------------------------------------------- edge cases
+
+def test_edge_root_only_and_errors(gpu):
+    """Single-token beams collapse; a bad explicit parent raises the device bit."""
+    inp = synth.make_inputs(0, 300)
+    inp["beams"][:] = inp["beams"][:, :1, :]          # all beams identical: a chain
+    tr = oracle_tree(inp)
+    step = pipeline.Step(inp, "reject_path")
+    res = step.run()
+    assert_tree_equal(res, tr)
+    assert res["n_nodes"][0] == 1 + inp["L"]
+    assert_verify_equal(res, oracle_verify(inp, tr, "reject_path"), "chain tree")
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    attn_bar(res["attn"], ref, "chain tree")
+
+    inp4 = synth.make_inputs(4, 300, B_override=2, ctx_override=100)
+    inp4["cand_parent"] = inp4["cand_parent"].copy()
+    inp4["cand_parent"][1, 5] = 9                      # candidate 5 names a later node
+    step = pipeline.Step(inp4, "reject_recursive")
+    res = step.run()
+    assert res["n_nodes"][1] == 1 and res["n_nodes"][0] == 49
+    assert res["status"] & 0x1
+    assert res["acc_len"][1] == 0

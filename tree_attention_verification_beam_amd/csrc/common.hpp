@@ -1,0 +1,73 @@
+// common.hpp -- device and host helpers shared by the library's HIP sources.
+// gfx950 only: 64-wide wavefronts, bf16 MFMA, 160 KB LDS per CU.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/specverify.h"
+
+namespace spec {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- status word
+__device__ inline void raise_status(int32_t* status, int32_t bits) {
+  if (status) atomicOr(status, bits);
+}
+
+// ---------------------------------------------------------------- reductions
+__device__ inline float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ inline float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// (value, index) maximum: larger value wins; equal values keep the lower index.
+__device__ inline void argmax_merge(float& m, int& a, float m2, int a2) {
+  if (m2 > m || (m2 == m && a2 < a)) {
+    m = m2;
+    a = a2;
+  }
+}
+
+__device__ inline void wave_argmax(float& m, int& a) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float m2 = __shfl_xor(m, o, kWave);
+    int a2 = __shfl_xor(a, o, kWave);
+    argmax_merge(m, a, m2, a2);
+  }
+}
+
+// ---------------------------------------------------------------- host side
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // namespace spec

@@ -1,0 +1,133 @@
+// kv_compact.hip -- commit the accepted path's K/V into contiguous cache slots.
+//
+// "Recurrent Drafter for Fast Speculative Decoding in Large Language Models",
+// section "The Full Speculative Decoding Loop", Step 6: the accepted tokens are
+// appended to the context and the next step starts after them.  The tree's K/V
+// sit at slots ctx + node; the accepted path's entries move to ctx + 1.., the
+// root staying at ctx.  A destination can be another entry's source
+// (path [0, 2, 3]: slot ctx+2 is both), so a workgroup first gathers all of
+// one head's moved rows into LDS, then scatters them.
+//
+// One workgroup per sequence walks its KV heads, K then V; the sequence's
+// ctx_len is updated by the same workgroup after the last move, so no other
+// workgroup reads it afterwards.
+#include "common.hpp"
+
+namespace spec {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_kv_compact(
+    int elem_bytes, int Hkv, int D, int cache_cap, int T_cap, unsigned char* __restrict__ kc,
+    unsigned char* __restrict__ vc, int32_t* __restrict__ ctx_len,
+    const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path,
+    int32_t* __restrict__ status) {
+  extern __shared__ __align__(16) unsigned char buf[];  // [T_cap][row bytes]
+  __shared__ int s_src[SPEC_MAX_TREE];
+  __shared__ int s_ok;
+  const int b = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int ctx = ctx_len[b];
+  const int n = acc_len[b];
+  const int32_t* path = acc_path + (size_t)b * T_cap;
+  if (tid == 0) s_ok = (n >= 0 && n < T_cap && ctx >= 0 && ctx + n + 1 <= cache_cap) ? 1 : 0;
+  __syncthreads();
+  if (s_ok) {
+    for (int i = 1 + tid; i <= n; i += kThreads) {
+      const int src = path[i];
+      // node ids along a path increase strictly and are at least their depth
+      if (src < i || ctx + src >= cache_cap || (i > 1 && src <= path[i - 1])) atomicAnd(&s_ok, 0);
+      s_src[i] = src;
+    }
+  }
+  __syncthreads();
+  if (!s_ok) {
+    if (tid == 0) raise_status(status, SPEC_DEV_CTX_RANGE);
+    return;
+  }
+  // rows that actually move
+  const int row16 = D * elem_bytes / 16;  // 16-byte words per row
+  for (int g = 0; g < Hkv; ++g) {
+    for (int which = 0; which < 2; ++which) {
+      unsigned char* base = (which ? vc : kc) + ((size_t)b * Hkv + g) * cache_cap * D * elem_bytes;
+      // gather
+      for (int e = tid; e < n * row16; e += kThreads) {
+        const int i = 1 + e / row16, w = e - (e / row16) * row16;
+        const int src = s_src[i];
+        if (src == i) continue;
+        reinterpret_cast<uint4*>(buf)[(size_t)(i - 1) * row16 + w] =
+            reinterpret_cast<const uint4*>(base + (size_t)(ctx + src) * D * elem_bytes)[w];
+      }
+      __syncthreads();
+      // scatter
+      for (int e = tid; e < n * row16; e += kThreads) {
+        const int i = 1 + e / row16, w = e - (e / row16) * row16;
+        if (s_src[i] == i) continue;
+        reinterpret_cast<uint4*>(base + (size_t)(ctx + i) * D * elem_bytes)[w] =
+            reinterpret_cast<const uint4*>(buf)[(size_t)(i - 1) * row16 + w];
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) ctx_len[b] = ctx + n + 1;
+}
+
+// Plain streaming copy, 16 bytes per thread per step, grid-stride.
+__global__ __launch_bounds__(256) void k_copy_probe(const uint4* __restrict__ src,
+                                                    uint4* __restrict__ dst, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    dst[i] = src[i];
+}
+
+}  // namespace
+}  // namespace spec
+
+using namespace spec;
+
+extern "C" int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int T_cap,
+                               void* k_cache, void* v_cache, int32_t* ctx_len,
+                               const int32_t* acc_len, const int32_t* acc_path, int32_t* status,
+                               void* stream) {
+  if (B < 0 || Hkv < 1 || D < 1 || cache_cap < 1 || T_cap < 1) return SPEC_ERR_INVALID;
+  if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
+  const int eb = dt == SPEC_F32 ? 4 : dt == SPEC_BF16 ? 2 : 0;
+  if (!eb) return SPEC_ERR_INVALID;
+  if ((D * eb) % 16) return SPEC_ERR_UNSUPPORTED;
+  if (B == 0) return SPEC_OK;
+  if (!k_cache || !v_cache || !ctx_len || !acc_len || !acc_path) return SPEC_ERR_INVALID;
+  if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return SPEC_ERR_INVALID;
+  const size_t lds = (size_t)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb;
+  if (lds > 64 * 1024) return SPEC_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(k_kv_compact, dim3(B), dim3(kThreads), lds, as_stream(stream), eb, Hkv, D,
+                     cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
+                     static_cast<unsigned char*>(v_cache), ctx_len, acc_len, acc_path, status);
+  return launch_status();
+}
+
+extern "C" int spec_copy_probe(const void* src, void* dst, size_t n_bytes, void* stream) {
+  if (!src || !dst || n_bytes % 16 || !aligned(src, 16) || !aligned(dst, 16))
+    return SPEC_ERR_INVALID;
+  if (n_bytes == 0) return SPEC_OK;
+  const size_t n16 = n_bytes / 16;
+  size_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_copy_probe, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  return launch_status();
+}
+
+extern "C" int spec_version(void) { return 100; }
+
+extern "C" const char* spec_status_string(int status) {
+  switch (status) {
+    case SPEC_OK: return "SPEC_OK";
+    case SPEC_ERR_INVALID: return "SPEC_ERR_INVALID";
+    case SPEC_ERR_UNSUPPORTED: return "SPEC_ERR_UNSUPPORTED";
+    case SPEC_ERR_CAPACITY: return "SPEC_ERR_CAPACITY";
+    case SPEC_ERR_WORKSPACE: return "SPEC_ERR_WORKSPACE";
+    case SPEC_ERR_HIP: return "SPEC_ERR_HIP";
+    default: return "SPEC_ERR_UNKNOWN";
+  }
+}

@@ -1,0 +1,920 @@
+// verify.hip -- acceptance, selection and residual resampling over the packed tree.
+//
+// "Recurrent Drafter for Fast Speculative Decoding in Large Language Models",
+// section "The Full Speculative Decoding Loop", Step 5: token matches (greedy)
+// or rejection sampling per token; the longest accepted prefix over all
+// candidates wins.  ResiSpec (paperpeel 2608.24411), section 4: candidates of
+// one position are checked in order, and after each rejection the target
+// becomes the residual max(0, p - q) / sum max(0, p - q).
+//
+// Kernels, in stream order:
+//   k_vprep   one workgroup per sequence: validates the tree against V and R,
+//             marks which draft rows are needed, resets the sequence's
+//             cross-workgroup counter.
+//   k_vstats  the vocabulary stream: every needed logits row is read once, in
+//             chunks; each chunk yields (max, argmax with the lowest index on
+//             ties, sum exp(l - max)).  Coalesced 16-byte loads; exp in fp32,
+//             sums in fp64.
+//   k_vselect P workgroups per sequence (P = 1 for greedy): merge the chunk
+//             partials into row statistics, gather p and q of every node's own
+//             token (fp64 exp), run the mode's tests and the path select, and
+//             do the residual passes and the inverse-CDF draw over the stop
+//             row pair in fp64.  With P > 1 the workgroups of a sequence split
+//             the vocabulary, publish per-pass partial sums and meet at a
+//             counter barrier; every workgroup then holds the same totals and
+//             takes the same decisions.  Such launches are cooperative, so all
+//             workgroups are resident; every wait is bounded.
+#include "common.hpp"
+
+namespace spec {
+namespace {
+
+constexpr int kStatThreads = 256;
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kMaxP = 32;
+constexpr size_t kSyncStride = 2048;  // bytes of sync area per sequence
+constexpr double kNearTie = 1e-5;
+constexpr double kCdfNearTie = 1e-9;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Partial {
+  double S;  // sum of exp(l - m) over the chunk
+  float m;   // chunk maximum
+  int arg;   // lowest index attaining m
+};
+
+struct VerifyPlan {
+  int ept;       // floats per thread in k_vstats
+  int chunk;     // floats per chunk
+  int n_chunks;  // chunks per row
+  long n_units;  // rows: B*T_cap target rows, then B*R draft rows
+  size_t off_part, off_need, off_bad, off_sync, total;
+};
+
+VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
+  VerifyPlan p{};
+  const int Rr = mode == SPEC_GREEDY ? 0 : R;
+  p.n_units = (long)B * T_cap + (long)B * Rr;
+  p.ept = 32;
+  while (p.ept > 4 && p.n_units * ((V + p.ept * kStatThreads - 1) / (p.ept * kStatThreads)) < 2048)
+    p.ept >>= 1;
+  p.chunk = p.ept * kStatThreads;
+  p.n_chunks = (V + p.chunk - 1) / p.chunk;
+  size_t off = 0;
+  p.off_part = off;
+  off += round_up((size_t)p.n_units * p.n_chunks * sizeof(Partial), 256);
+  p.off_need = off;
+  off += round_up((size_t)B * (Rr > 0 ? Rr : 1) * sizeof(int32_t), 256);
+  p.off_bad = off;
+  off += round_up((size_t)B * sizeof(int32_t), 256);
+  p.off_sync = off;
+  off += (size_t)B * kSyncStride;
+  p.total = off;
+  return p;
+}
+
+// ------------------------------------------------------------------ block reductions
+
+__device__ double block_sum_f64(double v, double* s_red) {
+  v = wave_sum_f64(v);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kSelWaves; ++w) t += s_red[w];
+  return t;
+}
+
+// two sums at once
+__device__ void block_sum2_f64(double& a, double& b, double* s_red) {
+  a = wave_sum_f64(a);
+  b = wave_sum_f64(b);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) {
+    s_red[wave] = a;
+    s_red[kSelWaves + wave] = b;
+  }
+  __syncthreads();
+  double ta = 0.0, tb = 0.0;
+  for (int w = 0; w < kSelWaves; ++w) {
+    ta += s_red[w];
+    tb += s_red[kSelWaves + w];
+  }
+  a = ta;
+  b = tb;
+}
+
+// exclusive scan over the block's threads (in thread order), fp64; returns the total
+__device__ double block_exclusive_scan_f64(double v, double* s_buf, double& excl) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  s_buf[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < kSelThreads; off <<= 1) {
+    const double add = tid >= off ? s_buf[tid - off] : 0.0;
+    __syncthreads();
+    s_buf[tid] += add;
+    __syncthreads();
+  }
+  excl = s_buf[tid] - v;
+  const double total = s_buf[kSelThreads - 1];
+  __syncthreads();
+  return total;
+}
+
+// ------------------------------------------------------------------ k_vprep
+
+__global__ __launch_bounds__(SPEC_MAX_TREE) void k_vprep(
+    int mode, int T_cap, int V, int R, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
+    const int32_t* __restrict__ depth, const int32_t* __restrict__ dft_row,
+    int32_t* __restrict__ need, int32_t* __restrict__ seq_bad, unsigned char* __restrict__ sync,
+    int32_t* __restrict__ status) {
+  __shared__ int s_has_child[SPEC_MAX_TREE];
+  __shared__ int s_bad;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int T = n_nodes[b];
+  const int Rr = mode == SPEC_GREEDY ? 0 : R;
+  if (t == 0) s_bad = 0;
+  s_has_child[t] = 0;
+  for (int r = t; r < Rr; r += SPEC_MAX_TREE) need[(size_t)b * Rr + r] = 0;
+  __syncthreads();
+  if (T < 1 || T > T_cap) {
+    if (t == 0) {
+      s_bad = SPEC_DEV_BAD_TREE;
+    }
+  } else if (t < T) {
+    const size_t i = (size_t)b * T_cap + t;
+    if (t > 0) {
+      const int p = parent[i];
+      if (p < 0 || p >= t) {
+        atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+      } else {
+        const int dp = p == 0 ? 0 : depth[(size_t)b * T_cap + p];
+        if (depth[i] != dp + 1) atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+        s_has_child[p] = 1;
+      }
+      const int x = token[i];
+      if (x < 0 || x >= V) atomicOr(&s_bad, SPEC_DEV_BAD_TOKEN);
+    }
+  }
+  __syncthreads();
+  if (Rr > 0 && !s_bad && t < T && s_has_child[t]) {
+    const int r = dft_row[(size_t)b * T_cap + t];
+    if (r < 0 || r >= Rr) atomicOr(&s_bad, SPEC_DEV_BAD_ROW);
+    else need[(size_t)b * Rr + r] = 1;
+  }
+  __syncthreads();
+  if (t == 0) {
+    seq_bad[b] = s_bad;
+    if (s_bad) raise_status(status, s_bad);
+    // reset the cross-workgroup counter of this sequence
+    __hip_atomic_store(reinterpret_cast<int*>(sync + (size_t)b * kSyncStride), 0, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ------------------------------------------------------------------ k_vstats
+
+template <int EPT, bool VEC>
+__global__ __launch_bounds__(kStatThreads) void k_vstats(
+    int B, int T_cap, int V, int Rr, int n_chunks, const float* __restrict__ tgt,
+    const float* __restrict__ dft, const int32_t* __restrict__ n_nodes,
+    const int32_t* __restrict__ need, Partial* __restrict__ part) {
+  __shared__ float s_m[kStatThreads / 64];
+  __shared__ int s_a[kStatThreads / 64];
+  __shared__ double s_s[kStatThreads / 64];
+  const long unit = blockIdx.x / n_chunks;
+  const int c = blockIdx.x - (int)(unit * n_chunks);
+  const float* row;
+  const long n_tgt = (long)B * T_cap;
+  if (unit < n_tgt) {
+    const int b = (int)(unit / T_cap), t = (int)(unit - (long)b * T_cap);
+    if (t > 0 && t >= n_nodes[b]) return;
+    row = tgt + unit * (long)V;
+  } else {
+    const long u2 = unit - n_tgt;
+    if (!need[u2]) return;
+    row = dft + u2 * (long)V;
+  }
+  const int tid = threadIdx.x;
+  const int base = c * EPT * kStatThreads;
+  float x[EPT];
+  int idx0[EPT / 4];
+  if constexpr (VEC) {
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const int e = base + 4 * (tid + kStatThreads * j);
+      idx0[j] = e;
+      f32x4 v4 = e < V ? *reinterpret_cast<const f32x4*>(row + e)
+                       : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      x[4 * j] = v4[0];
+      x[4 * j + 1] = v4[1];
+      x[4 * j + 2] = v4[2];
+      x[4 * j + 3] = v4[3];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j) {
+      const int e = base + 4 * (tid + kStatThreads * j);
+      idx0[j] = e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] = e + i < V ? row[e + i] : -INFINITY;
+    }
+  }
+  // local max / argmax in increasing index order
+  // (a stays INT_MAX until the first valid element, which is always taken)
+  float m = -INFINITY;
+  int a = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < EPT / 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (idx0[j] + i < V && (a == 0x7fffffff || x[4 * j + i] > m)) {
+        m = x[4 * j + i];
+        a = idx0[j] + i;
+      }
+  wave_argmax(m, a);
+  const int wave = tid >> 6, lane = tid & 63;
+  if (lane == 0) {
+    s_m[wave] = m;
+    s_a[wave] = a;
+  }
+  __syncthreads();
+  m = s_m[0];
+  a = s_a[0];
+  for (int w = 1; w < kStatThreads / 64; ++w) argmax_merge(m, a, s_m[w], s_a[w]);
+  // sum of exp(l - m): exp in fp32 (v_exp_f32 on the log2 argument), sums in fp64
+  float loc = 0.0f;
+  const float mb = m * kLog2e;
+#pragma unroll
+  for (int j = 0; j < EPT / 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (idx0[j] + i < V) loc += __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * j + i], kLog2e, -mb));
+  double s = wave_sum_f64((double)loc);
+  if (lane == 0) s_s[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    for (int w = 0; w < kStatThreads / 64; ++w) tot += s_s[w];
+    Partial p;
+    p.S = tot;
+    p.m = m;
+    p.arg = a;
+    part[unit * n_chunks + c] = p;
+  }
+}
+
+// ------------------------------------------------------------------ k_vselect
+
+struct SelArgs {
+  int B, T_cap, V, Rr, n_chunks, P;
+  const float* tgt;
+  const float* dft;
+  const int32_t* dft_row;
+  const int32_t* n_nodes;
+  const int32_t* parent;
+  const int32_t* token;
+  const int32_t* depth;
+  const float* u_node;
+  const float* u_final;
+  const Partial* part;
+  const int32_t* seq_bad;
+  unsigned char* sync;
+  int32_t* acc_len;
+  int32_t* acc_path;
+  int32_t* next_token;
+  float* p_tok;
+  float* q_tok;
+  int8_t* decision;
+  int32_t* near_tie;
+  int32_t* status;
+};
+
+// Shared state of one sequence inside a select workgroup.
+struct SelShared {
+  int par[SPEC_MAX_TREE];
+  int tok[SPEC_MAX_TREE];
+  int dep[SPEC_MAX_TREE];
+  int nch[SPEC_MAX_TREE];
+  int arg_p[SPEC_MAX_TREE];
+  float m_p[SPEC_MAX_TREE];
+  float m_q[SPEC_MAX_TREE];
+  double S_p[SPEC_MAX_TREE];
+  double S_q[SPEC_MAX_TREE];
+  double pt[SPEC_MAX_TREE];
+  double qt[SPEC_MAX_TREE];
+  int dec[SPEC_MAX_TREE];
+  int chain[SPEC_MAX_TREE];
+  double red[2 * kSelWaves];
+  double scan[kSelThreads];
+  double slots[2 * kMaxP];
+  double invN[64];
+  int near_count;
+  int stop;
+};
+
+// Cross-workgroup meeting point of the P workgroups of one sequence.
+struct SeqSync {
+  int* counter;
+  double* slot;  // [2 parities][kMaxP][2]
+  int P, w, rounds;
+  int32_t* status;
+
+  __device__ void publish(double a, double b) {
+    // called by thread 0 only
+    double* s = slot + ((rounds & 1) * kMaxP + w) * 2;
+    __hip_atomic_store(s, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(s + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Everyone publishes (a, b), waits for the other workgroups and returns the
+  // per-workgroup values in s_slots (identical in every workgroup).
+  __device__ void exchange(double a, double b, double* s_slots) {
+    if (P == 1) {
+      if (threadIdx.x == 0) {
+        s_slots[0] = a;
+        s_slots[1] = b;
+      }
+      __syncthreads();
+      ++rounds;
+      return;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      publish(a, b);
+      __atomic_thread_fence(__ATOMIC_RELEASE);
+      __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      const int target = P * (rounds + 1);
+      int spins = 0;
+      while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins > (1 << 24)) {
+          raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
+          break;
+        }
+      }
+      const double* src = slot + (rounds & 1) * kMaxP * 2;
+      for (int i = 0; i < 2 * P; ++i)
+        s_slots[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    ++rounds;
+  }
+};
+
+// One row pair (target row of node s and its draft row) with its statistics.
+struct RowPair {
+  const float* lp;
+  const float* lq;
+  double mp, mq;
+  double invSp, invSq;  // accurate (fp64) normalisers once known
+};
+
+// p(v), q(v) and the residual after k rejections, r_k(v), in fp64.
+__device__ inline double eval_r(const RowPair& rp, int v, int k, const double* invN, double& qv) {
+  double r = exp((double)rp.lp[v] - rp.mp) * rp.invSp;
+  qv = exp((double)rp.lq[v] - rp.mq) * rp.invSq;
+  for (int j = 0; j < k; ++j) {
+    const double w = r - qv;
+    r = w > 0.0 ? w * invN[j] : 0.0;
+  }
+  return r;
+}
+
+// Weight of v in the final draw: unnormalised p (k < 0) or max(0, r_k - q).
+__device__ inline double draw_weight(const RowPair& rp, int v, int k, const double* invN) {
+  if (k < 0) return exp((double)rp.lp[v] - rp.mp);
+  double qv;
+  const double r = eval_r(rp, v, k, invN, qv);
+  const double w = r - qv;
+  return w > 0.0 ? w : 0.0;
+}
+
+struct Slice {
+  int lo, hi;
+};
+
+__device__ inline Slice slice_of(int V, int P, int w) {
+  Slice s;
+  s.lo = (int)((long)V * w / P);
+  s.hi = (int)((long)V * (w + 1) / P);
+  return s;
+}
+
+// Accurate softmax normalisers of a row pair: sum exp(l - m) in fp64 over V.
+__device__ void pass_normalisers(RowPair& rp, bool with_q, SeqSync& sy, SelShared& sh, int V) {
+  const Slice sl = slice_of(V, sy.P, sy.w);
+  double a = 0.0, b = 0.0;
+  for (int v = sl.lo + threadIdx.x; v < sl.hi; v += kSelThreads) {
+    a += exp((double)rp.lp[v] - rp.mp);
+    if (with_q) b += exp((double)rp.lq[v] - rp.mq);
+  }
+  block_sum2_f64(a, b, sh.red);
+  sy.exchange(a, b, sh.slots);
+  double ta = 0.0, tb = 0.0;
+  for (int i = 0; i < sy.P; ++i) {
+    ta += sh.slots[2 * i];
+    tb += sh.slots[2 * i + 1];
+  }
+  rp.invSp = 1.0 / ta;
+  if (with_q) rp.invSq = 1.0 / tb;
+  __syncthreads();
+}
+
+// Normaliser of the next residual: sum_v max(0, r_k(v) - q(v)).
+__device__ double pass_residual_mass(const RowPair& rp, int k, const double* invN, SeqSync& sy,
+                                     SelShared& sh, int V) {
+  const Slice sl = slice_of(V, sy.P, sy.w);
+  double a = 0.0;
+  for (int v = sl.lo + threadIdx.x; v < sl.hi; v += kSelThreads) {
+    double qv;
+    const double r = eval_r(rp, v, k, invN, qv);
+    const double w = r - qv;
+    if (w > 0.0) a += w;
+  }
+  a = block_sum_f64(a, sh.red);
+  sy.exchange(a, 0.0, sh.slots);
+  double t = 0.0;
+  for (int i = 0; i < sy.P; ++i) t += sh.slots[2 * i];
+  __syncthreads();
+  return t;
+}
+
+// Inverse-CDF draw over draw_weight(.., k, ..) in ascending vocabulary order.
+// Each thread owns a contiguous range of its workgroup's slice.  Returns true in
+// the one workgroup that found the token (written to *out_tok / *out_near);
+// *total_out gets the total weight (all workgroups).
+__device__ bool pass_draw(const RowPair& rp, int k, const double* invN, double u, SeqSync& sy,
+                          SelShared& sh, int V, int* out_tok, int* out_near, double* total_out) {
+  const Slice sl = slice_of(V, sy.P, sy.w);
+  const int n = sl.hi - sl.lo;
+  const int per = (n + kSelThreads - 1) / kSelThreads;
+  const int t0 = sl.lo + threadIdx.x * per;
+  const int t1 = min(sl.hi, t0 + per);
+  double mine = 0.0;
+  for (int v = t0; v < t1; ++v) mine += draw_weight(rp, v, k, invN);
+  double excl;
+  const double slice_total = block_exclusive_scan_f64(mine, sh.scan, excl);
+  sy.exchange(slice_total, 0.0, sh.slots);
+  double total = 0.0;
+  for (int i = 0; i < sy.P; ++i) total += sh.slots[2 * i];
+  *total_out = total;
+  if (!(total > 0.0)) {
+    __syncthreads();
+    return false;
+  }
+  const double thr = u * total;
+  const double eps = kCdfNearTie * total;
+  // the slice holding the threshold (or, past the end, the last slice with weight)
+  double base = 0.0;
+  int js = -1, jlast = -1;
+  double base_last = 0.0;
+  for (int i = 0; i < sy.P; ++i) {
+    const double ti = sh.slots[2 * i];
+    if (ti > 0.0) {
+      jlast = i;
+      base_last = base;
+    }
+    if (js < 0 && ti > 0.0 && base + ti > thr) js = i;
+    if (js < 0) base += ti;
+  }
+  const bool overshoot = js < 0;
+  if (overshoot) {
+    js = jlast;
+    base = base_last;
+  }
+  __syncthreads();
+  if (js != sy.w) return false;
+  // the thread holding the threshold
+  __shared__ int s_found_tok, s_found_near;
+  if (threadIdx.x == 0) {
+    s_found_tok = -1;
+    s_found_near = 0;
+  }
+  __syncthreads();
+  // thread ranges [base + incl[t-1], base + incl[t]) partition the slice exactly
+  const double lo_run = base + (threadIdx.x > 0 ? sh.scan[threadIdx.x - 1] : 0.0);
+  const double hi_run = base + sh.scan[threadIdx.x];
+  (void)excl;
+  if (!overshoot && mine > 0.0 && lo_run <= thr && thr < hi_run) {
+    double run = lo_run;
+    int found = -1, last_pos = -1, near = 1;
+    for (int v = t0; v < t1; ++v) {
+      const double w = draw_weight(rp, v, k, invN);
+      if (!(w > 0.0)) continue;
+      last_pos = v;
+      const double before = run;
+      run += w;
+      if (run > thr) {
+        found = v;
+        near = (fabs(run - thr) < eps || fabs(before - thr) < eps) ? 1 : 0;
+        break;
+      }
+    }
+    s_found_tok = found >= 0 ? found : last_pos;
+    s_found_near = near;
+  }
+  __syncthreads();
+  if (s_found_tok < 0) {
+    // overshoot through rounding: the last token with positive weight of this slice
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = -1;
+    __syncthreads();
+    int last = -1;
+    for (int v = t0; v < t1; ++v)
+      if (draw_weight(rp, v, k, invN) > 0.0) last = v;
+    if (last >= 0) atomicMax(&s_last, last);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      s_found_tok = s_last < 0 ? sl.lo : s_last;
+      s_found_near = 1;
+    }
+    __syncthreads();
+  }
+  *out_tok = s_found_tok;
+  *out_near = s_found_near;
+  return true;
+}
+
+// merge the chunk partials of one row: max, lowest argmax, sum rescaled (fp64)
+__device__ inline void merge_row(const Partial* p, int n_chunks, float& m, int& arg, double& S) {
+  m = -INFINITY;
+  arg = 0;
+  for (int c = 0; c < n_chunks; ++c)
+    if (p[c].m > m) {
+      m = p[c].m;
+      arg = p[c].arg;
+    }
+  S = 0.0;
+  for (int c = 0; c < n_chunks; ++c)
+    if (p[c].m != -INFINITY) S += p[c].S * exp((double)p[c].m - (double)m);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
+  __shared__ SelShared sh;
+  const int b = blockIdx.x / A.P;
+  const int w = blockIdx.x - b * A.P;
+  const int tid = threadIdx.x;
+  const int T_cap = A.T_cap, V = A.V;
+  SeqSync sy;
+  sy.counter = reinterpret_cast<int*>(A.sync + (size_t)b * kSyncStride);
+  sy.slot = reinterpret_cast<double*>(A.sync + (size_t)b * kSyncStride + 64);
+  sy.P = A.P;
+  sy.w = w;
+  sy.rounds = 0;
+  sy.status = A.status;
+  const bool lead = w == 0;
+
+  const bool bad = A.seq_bad[b] != 0;
+  const int T = bad ? 1 : A.n_nodes[b];
+  const size_t nb = (size_t)b * T_cap;
+
+  // ---------------------------------------------------------------- tree + row stats
+  for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) {
+    sh.nch[t] = 0;
+    sh.dec[t] = -1;
+    sh.pt[t] = 0.0;
+    sh.qt[t] = 0.0;
+  }
+  if (tid == 0) sh.near_count = 0;
+  __syncthreads();
+  for (int t = tid; t < T; t += kSelThreads) {
+    sh.par[t] = t == 0 ? -1 : A.parent[nb + t];
+    sh.tok[t] = A.token[nb + t];
+    sh.dep[t] = t == 0 ? 0 : A.depth[nb + t];
+  }
+  __syncthreads();
+  for (int t = tid + 1; t < T; t += kSelThreads) atomicAdd(&sh.nch[sh.par[t]], 1);
+  for (int t = tid; t < T; t += kSelThreads) {
+    float m;
+    int arg;
+    double S;
+    merge_row(A.part + (nb + t) * A.n_chunks, A.n_chunks, m, arg, S);
+    sh.m_p[t] = m;
+    sh.arg_p[t] = arg;
+    sh.S_p[t] = S;
+  }
+  __syncthreads();
+  if (MODE != SPEC_GREEDY) {
+    for (int t = tid; t < T; t += kSelThreads) {
+      if (sh.nch[t] == 0) continue;
+      const int r = A.dft_row[nb + t];
+      float m;
+      int arg;
+      double S;
+      merge_row(A.part + ((size_t)A.B * T_cap + (size_t)b * A.Rr + r) * A.n_chunks, A.n_chunks, m,
+                arg, S);
+      sh.m_q[t] = m;
+      sh.S_q[t] = S;
+    }
+    __syncthreads();
+  }
+  // p and q of every node's own token under its parent (fp64 exp, merged sums)
+  for (int t = tid + 1; t < T; t += kSelThreads) {
+    const int s = sh.par[t], x = sh.tok[t];
+    const double lp = A.tgt[(nb + s) * V + x];
+    sh.pt[t] = exp(lp - (double)sh.m_p[s]) / sh.S_p[s];
+    if (MODE != SPEC_GREEDY) {
+      const int r = A.dft_row[nb + s];
+      const double lq = A.dft[((size_t)b * A.Rr + r) * V + x];
+      sh.qt[t] = exp(lq - (double)sh.m_q[s]) / sh.S_q[s];
+    }
+  }
+  __syncthreads();
+
+  int stop = 0;
+  // draw description for the final token
+  int draw_k = -1;          // -1: draw from p_stop; k >= 0: from max(0, r_k - q)
+  const double* invN = sh.invN;
+  RowPair rp{};
+
+  if (MODE == SPEC_GREEDY || MODE == SPEC_REJECT_PATH) {
+    for (int t = tid + 1; t < T; t += kSelThreads) {
+      int acc;
+      if (MODE == SPEC_GREEDY) {
+        acc = sh.tok[t] == sh.arg_p[sh.par[t]];
+      } else {
+        const double p = sh.pt[t], q = sh.qt[t];
+        const double ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
+        const double u = (double)A.u_node[nb + t];
+        acc = u < ratio;
+        if (fabs(ratio - u) < kNearTie) atomicAdd(&sh.near_count, 1);
+      }
+      sh.dec[t] = acc;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      sh.chain[0] = 1;
+      int best = 0;
+      for (int t = 1; t < T; ++t) {
+        sh.chain[t] = sh.dec[t] && sh.chain[sh.par[t]];
+        if (sh.chain[t] && sh.dep[t] > sh.dep[best]) best = t;
+      }
+      sh.stop = best;
+    }
+    __syncthreads();
+    stop = sh.stop;
+    if (MODE == SPEC_REJECT_PATH && !bad) {
+      rp.lp = A.tgt + (nb + stop) * V;
+      rp.mp = sh.m_p[stop];
+      if (sh.nch[stop] > 0) {
+        const int r = A.dft_row[nb + stop];
+        rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
+        rp.mq = sh.m_q[stop];
+        pass_normalisers(rp, true, sy, sh, V);
+        draw_k = 0;
+      }
+    }
+  } else {
+    // sequential multi-candidate verification with residual renormalisation
+    int s = 0;
+    for (;;) {
+      int k = 0;
+      draw_k = -1;
+      bool dead = false, have_norm = false, moved = false;
+      rp.lp = A.tgt + (nb + s) * V;
+      rp.mp = sh.m_p[s];
+      if (sh.nch[s] > 0) {
+        const int r = A.dft_row[nb + s];
+        rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
+        rp.mq = sh.m_q[s];
+      }
+      int remaining = sh.nch[s];
+      for (int ch = s + 1; ch < T && remaining > 0; ++ch) {
+        if (sh.par[ch] != s) continue;
+        --remaining;
+        if (dead) {
+          if (tid == 0) sh.dec[ch] = 0;
+          continue;
+        }
+        const int x = sh.tok[ch];
+        double ratio;
+        if (k == 0) {
+          const double p = sh.pt[ch], q = sh.qt[ch];
+          ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
+        } else {
+          double qv;
+          const double r = eval_r(rp, x, k, invN, qv);
+          ratio = qv > 0.0 ? r / qv : (r > 0.0 ? INFINITY : 0.0);
+        }
+        const double u = (double)A.u_node[nb + ch];
+        if (tid == 0 && fabs(ratio - u) < kNearTie) sh.near_count++;
+        if (u < ratio) {
+          if (tid == 0) sh.dec[ch] = 1;
+          s = ch;
+          moved = true;
+          break;
+        }
+        if (tid == 0) sh.dec[ch] = 0;
+        if (remaining == 0) {
+          // last child rejected: the draw uses max(0, r_k - q) unnormalised
+          if (!have_norm) pass_normalisers(rp, true, sy, sh, V);
+          draw_k = k;
+          break;
+        }
+        if (!have_norm) {
+          pass_normalisers(rp, true, sy, sh, V);
+          have_norm = true;
+        }
+        const double N = pass_residual_mass(rp, k, invN, sy, sh, V);
+        if (!(N > 0.0) || k >= 63) {
+          dead = true;
+          if (tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
+        } else {
+          if (tid == 0) sh.invN[k] = 1.0 / N;
+          __syncthreads();
+          ++k;
+        }
+      }
+      __syncthreads();
+      if (moved) continue;
+      stop = s;
+      if (dead) draw_k = -1;
+      break;
+    }
+  }
+
+  // ---------------------------------------------------------------- final token
+  int next = 0;
+  bool have_next = false;
+  int cdf_near = 0;
+  if (MODE == SPEC_GREEDY || bad) {
+    next = sh.arg_p[stop];
+    have_next = lead;
+  } else {
+    rp.lp = A.tgt + (nb + stop) * V;
+    rp.mp = sh.m_p[stop];
+    const double u = (double)A.u_final[b];
+    double total = 0.0;
+    int tok = 0, near = 0;
+    bool found = pass_draw(rp, draw_k, invN, u, sy, sh, V, &tok, &near, &total);
+    if (!(total > 0.0) && draw_k >= 0) {
+      // nothing left in the residual (rounding only): draw from p_stop
+      if (lead && tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
+      found = pass_draw(rp, -1, invN, u, sy, sh, V, &tok, &near, &total);
+    }
+    if (found) {
+      next = tok;
+      cdf_near = near;
+      have_next = true;
+    }
+  }
+
+  // ---------------------------------------------------------------- outputs
+  const int near_total = sh.near_count + cdf_near;
+  if (have_next && tid == 0) {
+    A.next_token[b] = next;
+    if (A.near_tie) A.near_tie[b] = near_total;
+  }
+  if (!lead) return;
+  if (tid == 0) A.acc_len[b] = sh.dep[stop];
+  for (int t = tid; t < T_cap; t += kSelThreads) {
+    int pv = -1;
+    if (!bad && t <= sh.dep[stop]) {
+      int cur = stop;
+      while (sh.dep[cur] > t) cur = sh.par[cur];
+      pv = cur;
+    }
+    if (bad && t == 0) pv = 0;
+    A.acc_path[nb + t] = pv;
+    if (A.decision) A.decision[nb + t] = (int8_t)((t < T && !bad) ? sh.dec[t] : -1);
+    if (A.p_tok) A.p_tok[nb + t] = (t < T && !bad) ? (float)sh.pt[t] : 0.0f;
+    if (A.q_tok) A.q_tok[nb + t] = (t < T && !bad) ? (float)sh.qt[t] : 0.0f;
+  }
+}
+
+// Largest P with B * P co-resident select workgroups, at most kMaxP, and at
+// least 2048 vocabulary entries per workgroup.
+int choose_p(int mode, int B, int V) {
+  if (mode == SPEC_GREEDY) return 1;
+  static int cached_capacity = -1;
+  static int cached_device = -1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (cached_device != dev) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_RECURSIVE>),
+            kSelThreads, 0) != hipSuccess)
+      return 1;
+    cached_capacity = cus * per_cu;
+    cached_device = dev;
+  }
+  int P = cached_capacity / (B > 0 ? B : 1);
+  const int by_v = V / 2048;
+  if (P > by_v) P = by_v;
+  if (P > kMaxP) P = kMaxP;
+  if (P < 1) P = 1;
+  return P;
+}
+
+template <int EPT>
+void launch_stats(const VerifyPlan& pl, bool vec, int B, int T_cap, int V, int Rr,
+                  const float* tgt, const float* dft, const int32_t* n_nodes, const int32_t* need,
+                  Partial* part, hipStream_t s) {
+  const dim3 grid((unsigned)(pl.n_units * pl.n_chunks));
+  if (vec)
+    hipLaunchKernelGGL((k_vstats<EPT, true>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
+                       pl.n_chunks, tgt, dft, n_nodes, need, part);
+  else
+    hipLaunchKernelGGL((k_vstats<EPT, false>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
+                       pl.n_chunks, tgt, dft, n_nodes, need, part);
+}
+
+}  // namespace
+}  // namespace spec
+
+using namespace spec;
+
+extern "C" size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R) {
+  if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE || B < 1 || T_cap < 1 || V < 1)
+    return 0;
+  return make_plan(mode, B, T_cap, V, R).total;
+}
+
+extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float* tgt,
+                           const float* dft, const int32_t* dft_row, const int32_t* n_nodes,
+                           const int32_t* parent, const int32_t* token, const int32_t* depth,
+                           const float* u_node, const float* u_final, int32_t* acc_len,
+                           int32_t* acc_path, int32_t* next_token, float* p_tok, float* q_tok,
+                           int8_t* decision, int32_t* near_tie, void* ws, size_t ws_bytes,
+                           int32_t* status, void* stream) {
+  if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE) return SPEC_ERR_INVALID;
+  if (B < 0 || T_cap < 1 || V < 1 || R < 0) return SPEC_ERR_INVALID;
+  if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
+  if (B == 0) return SPEC_OK;
+  if (!tgt || !n_nodes || !parent || !token || !depth || !acc_len || !acc_path || !next_token)
+    return SPEC_ERR_INVALID;
+  if (mode != SPEC_GREEDY) {
+    if (!dft || !dft_row || R < 1 || !u_node || !u_final) return SPEC_ERR_INVALID;
+  }
+  const VerifyPlan pl = make_plan(mode, B, T_cap, V, R);
+  if (!ws || ws_bytes < pl.total || !aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
+  const int Rr = mode == SPEC_GREEDY ? 0 : R;
+  char* w = static_cast<char*>(ws);
+  Partial* part = reinterpret_cast<Partial*>(w + pl.off_part);
+  int32_t* need = reinterpret_cast<int32_t*>(w + pl.off_need);
+  int32_t* seq_bad = reinterpret_cast<int32_t*>(w + pl.off_bad);
+  unsigned char* sync = reinterpret_cast<unsigned char*>(w + pl.off_sync);
+  hipStream_t s = as_stream(stream);
+
+  hipLaunchKernelGGL(k_vprep, dim3(B), dim3(SPEC_MAX_TREE), 0, s, mode, T_cap, V, Rr, n_nodes,
+                     parent, token, depth, dft_row, need, seq_bad, sync, status);
+  const bool vec = (V % 4 == 0) && aligned(tgt, 16) && (Rr == 0 || aligned(dft, 16));
+  switch (pl.ept) {
+    case 32: launch_stats<32>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
+    case 16: launch_stats<16>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
+    case 8: launch_stats<8>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
+    default: launch_stats<4>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
+  }
+  int rc = launch_status();
+  if (rc != SPEC_OK) return rc;
+
+  SelArgs A;
+  A.B = B;
+  A.T_cap = T_cap;
+  A.V = V;
+  A.Rr = Rr;
+  A.n_chunks = pl.n_chunks;
+  A.P = choose_p(mode, B, V);
+  A.tgt = tgt;
+  A.dft = dft;
+  A.dft_row = dft_row;
+  A.n_nodes = n_nodes;
+  A.parent = parent;
+  A.token = token;
+  A.depth = depth;
+  A.u_node = u_node;
+  A.u_final = u_final;
+  A.part = part;
+  A.seq_bad = seq_bad;
+  A.sync = sync;
+  A.acc_len = acc_len;
+  A.acc_path = acc_path;
+  A.next_token = next_token;
+  A.p_tok = p_tok;
+  A.q_tok = q_tok;
+  A.decision = decision;
+  A.near_tie = near_tie;
+  A.status = status;
+  const dim3 grid((unsigned)(B * A.P));
+  const void* fn = mode == SPEC_GREEDY ? reinterpret_cast<const void*>(k_vselect<SPEC_GREEDY>)
+                   : mode == SPEC_REJECT_PATH
+                       ? reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_PATH>)
+                       : reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_RECURSIVE>);
+  void* args[] = {&A};
+  hipError_t e;
+  if (A.P > 1)
+    e = hipLaunchCooperativeKernel(fn, grid, dim3(kSelThreads), args, 0, s);
+  else
+    e = hipLaunchKernel(fn, grid, dim3(kSelThreads), args, 0, s);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
