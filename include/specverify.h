@@ -204,7 +204,11 @@ int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, cons
  * safe); the root stays at slot ctx.  Then ctx_len[b] += acc_len[b] + 1 (the
  * root and the accepted tokens; next_token is the next step's root).
  * dt selects the element size; k_cache, v_cache [B][Hkv][cache_cap][D] in
- * place; ctx_len [B] in/out; acc_len [B], acc_path [B][T_cap] from spec_verify.
+ * place; ctx_len [B] in/out, each in [0, cache_cap); acc_len [B], acc_path
+ * [B][T_cap] from spec_verify.  Requires cache_cap < 2^24 and Hkv <= 63
+ * (SPEC_ERR_UNSUPPORTED otherwise): while the call runs, ctx_len[b] also
+ * counts the arriving workgroups in its top bits, so nothing else may read it
+ * until the call has finished on `stream`.
  * A path that is not increasing or leaves the cache raises SPEC_DEV_CTX_RANGE
  * and that sequence is left untouched.
  */

@@ -22,6 +22,20 @@ __device__ inline void raise_status(int32_t* status, int32_t bits) {
   if (status) atomicOr(status, bits);
 }
 
+// ---------------------------------------------------------------- cross-workgroup hand-over
+// The per-XCD L2 caches are not coherent with each other.  Agent-scope relaxed
+// atomic stores and loads reach the device-coherent level directly, so data
+// passed between workgroups of one kernel goes through these, and a writer
+// waits for its stores to complete (vmcnt) before it signals with an atomic;
+// no cache-wide write-back or invalidate is needed.
+__device__ inline void store_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint64_t load_coherent(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // ---------------------------------------------------------------- reductions
 __device__ inline float wave_max_f32(float v) {
 #pragma unroll

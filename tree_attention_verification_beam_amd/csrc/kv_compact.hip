@@ -7,32 +7,42 @@
 // root staying at ctx.  A destination can be another entry's source
 // (path [0, 2, 3]: slot ctx+2 is both), so a workgroup first gathers all of
 // one head's moved rows into LDS, then scatters them.
-//
-// One workgroup per sequence walks its KV heads, K then V; the sequence's
-// ctx_len is updated by the same workgroup after the last move, so no other
-// workgroup reads it afterwards.
 #include "common.hpp"
 
 namespace spec {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kArrive = 1 << 24;  // arrival count lives above the context length
 
+// One workgroup per (sequence, KV head, K or V).  Every workgroup of a sequence
+// first adds kArrive to ctx_len[b] atomically: the low 24 bits of the returned
+// value are the context length before the commit, whatever the arrival order,
+// and the workgroup that arrives last writes the new length (all others have
+// read the old one by then).
 __global__ __launch_bounds__(kThreads) void k_kv_compact(
     int elem_bytes, int Hkv, int D, int cache_cap, int T_cap, unsigned char* __restrict__ kc,
     unsigned char* __restrict__ vc, int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path,
     int32_t* __restrict__ status) {
-  extern __shared__ __align__(16) unsigned char buf[];  // [T_cap][row bytes]
+  extern __shared__ __align__(16) unsigned char buf[];  // [T_cap - 1][row bytes]
   __shared__ int s_src[SPEC_MAX_TREE];
-  __shared__ int s_ok;
+  __shared__ int s_ok, s_ctx, s_last;
   const int b = blockIdx.x;
+  const int g = blockIdx.y >> 1;
+  const int which = blockIdx.y & 1;
   const int tid = threadIdx.x;
-  const int ctx = ctx_len[b];
   const int n = acc_len[b];
   const int32_t* path = acc_path + (size_t)b * T_cap;
-  if (tid == 0) s_ok = (n >= 0 && n < T_cap && ctx >= 0 && ctx + n + 1 <= cache_cap) ? 1 : 0;
+  if (tid == 0) {
+    const int old = atomicAdd(ctx_len + b, kArrive);
+    const int ctx = old & (kArrive - 1);
+    s_ctx = ctx;
+    s_last = (old >> 24) == 2 * Hkv - 1;
+    s_ok = (n >= 0 && n < T_cap && ctx + n + 1 <= cache_cap) ? 1 : 0;
+  }
   __syncthreads();
+  const int ctx = s_ctx;
   if (s_ok) {
     for (int i = 1 + tid; i <= n; i += kThreads) {
       const int src = path[i];
@@ -42,35 +52,29 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
     }
   }
   __syncthreads();
-  if (!s_ok) {
-    if (tid == 0) raise_status(status, SPEC_DEV_CTX_RANGE);
-    return;
-  }
-  // rows that actually move
-  const int row16 = D * elem_bytes / 16;  // 16-byte words per row
-  for (int g = 0; g < Hkv; ++g) {
-    for (int which = 0; which < 2; ++which) {
-      unsigned char* base = (which ? vc : kc) + ((size_t)b * Hkv + g) * cache_cap * D * elem_bytes;
-      // gather
-      for (int e = tid; e < n * row16; e += kThreads) {
-        const int i = 1 + e / row16, w = e - (e / row16) * row16;
-        const int src = s_src[i];
-        if (src == i) continue;
-        reinterpret_cast<uint4*>(buf)[(size_t)(i - 1) * row16 + w] =
-            reinterpret_cast<const uint4*>(base + (size_t)(ctx + src) * D * elem_bytes)[w];
-      }
-      __syncthreads();
-      // scatter
-      for (int e = tid; e < n * row16; e += kThreads) {
-        const int i = 1 + e / row16, w = e - (e / row16) * row16;
-        if (s_src[i] == i) continue;
-        reinterpret_cast<uint4*>(base + (size_t)(ctx + i) * D * elem_bytes)[w] =
-            reinterpret_cast<const uint4*>(buf)[(size_t)(i - 1) * row16 + w];
-      }
-      __syncthreads();
+  if (s_ok) {
+    const int row16 = D * elem_bytes / 16;  // 16-byte words per row
+    unsigned char* base = (which ? vc : kc) + ((size_t)b * Hkv + g) * cache_cap * D * elem_bytes;
+    for (int e = tid; e < n * row16; e += kThreads) {
+      const int i = 1 + e / row16, w = e - (e / row16) * row16;
+      const int src = s_src[i];
+      if (src == i) continue;
+      reinterpret_cast<uint4*>(buf)[(size_t)(i - 1) * row16 + w] =
+          reinterpret_cast<const uint4*>(base + (size_t)(ctx + src) * D * elem_bytes)[w];
+    }
+    __syncthreads();
+    for (int e = tid; e < n * row16; e += kThreads) {
+      const int i = 1 + e / row16, w = e - (e / row16) * row16;
+      if (s_src[i] == i) continue;
+      reinterpret_cast<uint4*>(base + (size_t)(ctx + i) * D * elem_bytes)[w] =
+          reinterpret_cast<const uint4*>(buf)[(size_t)(i - 1) * row16 + w];
     }
   }
-  if (tid == 0) ctx_len[b] = ctx + n + 1;
+  if (tid == 0 && s_last) {
+    // every other workgroup of the sequence has read the old length already
+    atomicExch(ctx_len + b, s_ok ? ctx + n + 1 : ctx);
+    if (!s_ok) raise_status(status, SPEC_DEV_CTX_RANGE);
+  }
 }
 
 // Plain streaming copy, 16 bytes per thread per step, grid-stride.
@@ -95,13 +99,15 @@ extern "C" int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int
   const int eb = dt == SPEC_F32 ? 4 : dt == SPEC_BF16 ? 2 : 0;
   if (!eb) return SPEC_ERR_INVALID;
   if ((D * eb) % 16) return SPEC_ERR_UNSUPPORTED;
+  if (cache_cap >= kArrive) return SPEC_ERR_UNSUPPORTED;  // lengths share a word with a count
+  if (2 * Hkv > 127) return SPEC_ERR_UNSUPPORTED;
   if (B == 0) return SPEC_OK;
   if (!k_cache || !v_cache || !ctx_len || !acc_len || !acc_path) return SPEC_ERR_INVALID;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return SPEC_ERR_INVALID;
   const size_t lds = (size_t)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb;
   if (lds > 64 * 1024) return SPEC_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(k_kv_compact, dim3(B), dim3(kThreads), lds, as_stream(stream), eb, Hkv, D,
-                     cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
+  hipLaunchKernelGGL(k_kv_compact, dim3(B, 2 * Hkv), dim3(kThreads), lds, as_stream(stream), eb,
+                     Hkv, D, cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
                      static_cast<unsigned char*>(v_cache), ctx_len, acc_len, acc_path, status);
   return launch_status();
 }

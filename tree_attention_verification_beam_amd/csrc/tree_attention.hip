@@ -6,19 +6,25 @@
 // forward pass over the packed beam under the tree mask; each token's result
 // equals the one it would get had its own prefix been decoded token by token.
 // "Clover: Regressive Lightweight Speculative Decoding with Sequential
-// Knowledge", Figure 4: mask M_ij = 1 iff j is an ancestor of i or i = j.
+// Knowledge", causal mask construction: M_ij = 1 iff j is an ancestor of i or
+// i = j.
 //
 // bf16 path (gfx950 MFMA).  For one (sequence, KV head) the G query heads of the
 // group times the T tree nodes form an M = G*T row block that shares every key,
-// so Q K^T and P V are real dense contractions.  A workgroup of 4 waves owns a
-// slice of those rows (16-row MFMA tiles) and a slice of the keys: it streams
-// 64-key K and V tiles through LDS (double-buffered, V stored transposed so the
-// P V operand is a contiguous LDS read), computes S^T = K Q^T with
-// v_mfma_f32_16x16x32_bf16 so that each lane ends up owning one query row,
-// runs the online softmax in fp32 in exp2 form, and accumulates O^T = V^T P^T
-// with the same MFMA.  Context keys are unmasked; only the last tiles, which
-// hold the tree slots, test the ancestor bits.  Long contexts are split across
-// workgroups; a merge kernel combines the (max, sum, O) partials.
+// so Q K^T and P V are real dense contractions and every K/V byte is read once
+// for all of them.  A workgroup of NW waves owns a slice of those rows (QT
+// 16-row MFMA tiles per wave) and a range of keys: it streams 64-key K and V
+// tiles through LDS (double-buffered; V stored transposed so the P V operand is
+// a contiguous LDS read), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 so
+// that each lane owns one query row, runs the online softmax in fp32 in exp2
+// form, and accumulates O^T = V^T P^T with the same MFMA.  When few rows exist
+// (no GQA, small trees) the waves split each key tile instead (KG key groups)
+// and combine through LDS at the end.  The running maximum is only moved when
+// a score exceeds it by more than 2^8, so most tiles skip the rescale of the
+// accumulators; the result is the same softmax.  Context keys are unmasked;
+// only tiles that reach the tree slots test the ancestor bits.  Long contexts
+// are split across workgroups (chosen so the grid fills the 256 CUs evenly) and
+// a merge kernel combines the (max, sum, O) partials.
 //
 // fp32 path: one wavefront per output row, plain FMA, for the small fp32 case.
 #include "common.hpp"
@@ -27,49 +33,62 @@ namespace spec {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kKeyTile = 64;   // keys per LDS stage
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kKeyTile = 64;      // keys per LDS stage
+constexpr int kNumCU = 256;       // MI355X compute units
+constexpr int kMaxSplits = 32;    // context splits per (sequence, KV head)
+constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
 
 // ------------------------------------------------------------------ geometry
 
 struct AttnPlan {
-  int KG;        // key groups per workgroup (waves splitting a key tile)
+  int NW;        // waves per workgroup
   int QT;        // 16-row query tiles per wave
-  int n_mt;      // row tiles (workgroups) per (b, kv head)
+  int KG;        // key groups (waves splitting one key tile)
+  int PF;        // tiles of global loads in flight per workgroup (1 or 2)
+  int n_mt;      // row blocks (workgroups sharing one key range)
   int n_splits;  // context splits
   int tiles_per_split;
   int n_kv;      // B * Hkv * n_splits, the key-stream work units
   int n_slots;   // workgroups launched (n_kv padded to a multiple of 8, times n_mt)
 };
 
-AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
-  AttnPlan p{};
-  const int G = H / Hkv;
-  const int rows = G * T_cap;
-  const int nq = (rows + 15) / 16;
-  if (nq <= 4) {
-    p.KG = 2;
-    p.QT = (nq + 1) / 2;
-    p.n_mt = 1;
-  } else {
-    p.KG = 1;
-    p.QT = 2;
-    const int per_wg = 4 * p.QT;
-    p.n_mt = (nq + per_wg - 1) / per_wg;
-  }
-  const int total_keys = max_ctx + T_cap;
-  const int n_tiles = (total_keys + kKeyTile - 1) / kKeyTile;
-  const long base = (long)B * Hkv * p.n_mt;
-  int want = (int)((512 + base - 1) / base);
-  if (want < 1) want = 1;
-  // at least 4 tiles (256 keys) per split
-  int max_splits = (n_tiles + 3) / 4;
-  if (max_splits < 1) max_splits = 1;
-  if (want > max_splits) want = max_splits;
-  p.tiles_per_split = (n_tiles + want - 1) / want;
+void finish_plan(AttnPlan& p, int B, int T_cap, int H, int Hkv, int max_ctx, int want_splits) {
+  const int nq = (H / Hkv * T_cap + 15) / 16;
+  const int per_wg = p.NW / p.KG * p.QT;
+  p.n_mt = (nq + per_wg - 1) / per_wg;
+  const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
+  int s = want_splits < 1 ? 1 : want_splits;
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s > n_tiles) s = n_tiles;
+  p.tiles_per_split = (n_tiles + s - 1) / s;
   p.n_splits = (n_tiles + p.tiles_per_split - 1) / p.tiles_per_split;
   p.n_kv = B * Hkv * p.n_splits;
   p.n_slots = ((p.n_kv + 7) / 8) * 8 * p.n_mt;
+}
+
+// Shape-driven choice of the tiling: enough query tiles per wave to reuse each
+// K/V tile across the whole G*T row block, and enough context splits that the
+// busy workgroups cover every CU about once (or twice for 4-wave groups).
+AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
+  AttnPlan p{};
+  const int nq = (H / Hkv * T_cap + 15) / 16;
+  p.NW = 8;
+  if (nq <= 4) {
+    // few rows: waves pair up on each key tile (two key groups)
+    p.KG = 2; p.QT = 1; p.PF = 1;
+  } else if (nq <= 16) {
+    // one row block: two query tiles per wave, two tiles of loads in flight
+    p.KG = 1; p.QT = 2; p.PF = 2;
+  } else {
+    // many rows (wide GQA groups): 128-row blocks read the same key range
+    p.KG = 1; p.QT = 1; p.PF = 1;
+  }
+  const long units = (long)B * Hkv;
+  const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
+  long want = (kNumCU + units - 1) / units;
+  const long by_len = n_tiles / 2 > 0 ? n_tiles / 2 : 1;  // at least 2 tiles per split
+  if (want > by_len) want = by_len;
+  finish_plan(p, B, T_cap, H, Hkv, max_ctx, (int)want);
   return p;
 }
 
@@ -93,12 +112,34 @@ struct Lds {
   static constexpr int kBytes = 2 * kStage * 2;  // two stages of bf16
 };
 
+struct AttnArgs {
+  int B, T_cap, H, Hkv, cache_cap, max_ctx, n_splits, tiles_per_split, n_kv, n_mt;
+  float scale_log2;
+  const bf16_t* q;
+  const bf16_t* kc;
+  const bf16_t* vc;
+  const int32_t* ctx_len;
+  const int32_t* n_nodes;
+  const uint64_t* anc;
+  bf16_t* out;
+  float* part_o;
+  float* part_m;
+  float* part_l;
+  int32_t* status;
+};
+
 __device__ inline f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Map a workgroup slot to (kv unit, row tile) so that the row tiles sharing one
-// key stream land on the same XCD (slots are dealt round-robin over 8 XCDs).
+// Workgroup barrier for LDS hand-over: waits for this wave's LDS operations
+// only (not its outstanding global loads, which may stay in flight across it).
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Map a workgroup slot to (kv unit, row block) so that the row blocks sharing
+// one key stream land on the same XCD (slots are dealt round-robin over 8 XCDs).
 __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   const int xcd = slot & 7;
   const int j = slot >> 3;
@@ -106,30 +147,26 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
-template <int D, int QT, int KG>
-__global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
-    int B, int T_cap, int H, int Hkv, int cache_cap, int max_ctx, int n_splits,
-    int tiles_per_split, int n_kv, int n_mt, const bf16_t* __restrict__ q,
-    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
-    const int32_t* __restrict__ ctx_len, const int32_t* __restrict__ n_nodes,
-    const uint64_t* __restrict__ anc, float scale_log2, bf16_t* __restrict__ out,
-    float* __restrict__ part_o, float* __restrict__ part_m, float* __restrict__ part_l,
-    int32_t* __restrict__ status) {
-  constexpr int RG = 4 / KG;            // row groups
+template <int D, int NW, int QT, int KG, int PF>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
+  constexpr int kThreads = NW * 64;
+  constexpr int RG = NW / KG;           // row groups
   constexpr int KSTEPS = D / 32;        // k-steps of Q K^T
   constexpr int DT = D / 16;            // 16-wide d tiles of the output
   constexpr int KEYS_W = kKeyTile / KG; // keys per wave per tile
-  constexpr int SUB = KEYS_W / 16;      // 16-key sub-tiles per wave per tile
   constexpr int PV_STEPS = KEYS_W / 32; // 32-key k-steps of P V per tile
   static_assert(KG == 1 || KG == 2, "key groups");
+  static_assert(NW % KG == 0, "waves per key group");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   bf16_t* smem = reinterpret_cast<bf16_t*>(smem_raw);
 
   int kv_unit, mt;
-  slot_to_work(blockIdx.x, n_mt, kv_unit, mt);
-  if (kv_unit >= n_kv) return;
+  slot_to_work(blockIdx.x, a.n_mt, kv_unit, mt);
+  if (kv_unit >= a.n_kv) return;
+  const int n_splits = a.n_splits;
   const int sp = kv_unit % n_splits;
   const int bh = kv_unit / n_splits;
+  const int Hkv = a.Hkv, T_cap = a.T_cap, H = a.H;
   const int b = bh / Hkv;
   const int g_kv = bh - b * Hkv;
   const int G = H / Hkv;
@@ -144,16 +181,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
-  const int ctx = ctx_len[b];
-  const int T = n_nodes[b];
-  const bool bad = T < 1 || T > T_cap || ctx < 0 || ctx > max_ctx || ctx + T > cache_cap;
+  const int ctx = a.ctx_len[b];
+  const int T = a.n_nodes[b];
+  const bool bad =
+      T < 1 || T > T_cap || ctx < 0 || ctx > a.max_ctx || ctx + T > a.cache_cap;
   const int rows_valid = bad ? 0 : G * T;
   const int nq_valid = (rows_valid + 15) >> 4;
   const int n_keys = ctx + T;
-  const int k_begin = sp * tiles_per_split * kKeyTile;
-  int k_end = k_begin + tiles_per_split * kKeyTile;
+  const int k_begin = sp * a.tiles_per_split * kKeyTile;
+  int k_end = k_begin + a.tiles_per_split * kKeyTile;
   if (k_end > n_keys) k_end = n_keys;
-  if (bad && sp == 0 && mt == 0 && tid == 0) raise_status(status, SPEC_DEV_CTX_RANGE);
+  if (bad && sp == 0 && mt == 0 && tid == 0) raise_status(a.status, SPEC_DEV_CTX_RANGE);
 
   // this wave's query tiles: interleaved over the row groups of the workgroup
   int qt_idx[QT];
@@ -163,25 +201,24 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
     qt_idx[i] = mt * RG * QT + i * RG + rg;
     qt_on[i] = qt_idx[i] < nq_valid && k_begin < k_end;
   }
-  const int wg_first_q = mt * RG * QT * 16;
-  const bool wg_active = wg_first_q < rows_valid && k_begin < k_end;
+  const int wg_first_row = mt * RG * QT * 16;
+  const int wg_end_row = min(M_cap, wg_first_row + RG * QT * 16);
+  const bool wg_active = wg_first_row < rows_valid && k_begin < k_end;
 
   // ---------------------------------------------------------------- empty work
   if (!wg_active) {
     if (n_splits == 1) {
-      // zero the output rows of this row tile (padding nodes / bad sequences)
-      const int r0 = wg_first_q, r1 = min(M_cap, r0 + RG * QT * 16);
-      for (int e = tid; e < (r1 - r0) * D; e += kThreads) {
-        const int r = r0 + e / D, d = e % D;
+      // zero the output rows of this row block (padding nodes / bad sequences)
+      for (int e = tid; e < (wg_end_row - wg_first_row) * D; e += kThreads) {
+        const int r = wg_first_row + e / D, d = e % D;
         const int t = r / G, gq = r - t * G;
-        out[(((size_t)b * T_cap + t) * H + g_kv * G + gq) * D + d] = (bf16_t)0.0f;
+        a.out[(((size_t)b * T_cap + t) * H + g_kv * G + gq) * D + d] = (bf16_t)0.0f;
       }
     } else {
       const size_t ubase = (size_t)kv_unit * M_cap;
-      const int r0 = wg_first_q, r1 = min(M_cap, r0 + RG * QT * 16);
-      for (int r = r0 + tid; r < r1; r += kThreads) {
-        part_m[ubase + r] = -INFINITY;
-        part_l[ubase + r] = 0.0f;
+      for (int r = wg_first_row + tid; r < wg_end_row; r += kThreads) {
+        a.part_m[ubase + r] = -INFINITY;
+        a.part_l[ubase + r] = 0.0f;
       }
     }
     return;
@@ -197,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
     const int t = r / G;
     const int gq = r - t * G;
     const bool live = qt_on[i] && r < rows_valid;
-    const bf16_t* qrow = q + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
+    const bf16_t* qrow = a.q + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
       if (live) {
@@ -206,8 +243,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
         qf[i][s] = bf16x8{};
       }
     }
-    mask0[i] = live ? anc[((size_t)b * T_cap + t) * n_words] : 0ull;
-    mask1[i] = (live && n_words > 1) ? anc[((size_t)b * T_cap + t) * n_words + 1] : 0ull;
+    mask0[i] = live ? a.anc[((size_t)b * T_cap + t) * n_words] : 0ull;
+    mask1[i] = (live && n_words > 1) ? a.anc[((size_t)b * T_cap + t) * n_words + 1] : 0ull;
   }
 
   // ---------------------------------------------------------------- state
@@ -221,159 +258,151 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
     for (int d = 0; d < DT; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const bf16_t* kbase = kc + (size_t)bh * cache_cap * D;
-  const bf16_t* vbase = vc + (size_t)bh * cache_cap * D;
+  const bf16_t* kbase = a.kc + (size_t)bh * a.cache_cap * D;
+  const bf16_t* vbase = a.vc + (size_t)bh * a.cache_cap * D;
 
   // ---------------------------------------------------------------- tile loader
-  // K: 64 keys x D, unit = (key, 8-wide d octet); V: unit = (4 keys, d octet).
+  // K: 64 keys x D, unit = (key, 8-wide d octet); V: unit = (VK keys, d octet),
+  // sized so every thread owns exactly one V unit.  Key indices are clamped to
+  // the last key of the range: the loads never branch (a full and a partial
+  // tile run the same code, so prefetched loads stay in flight), and the keys
+  // past the range are masked to -inf before the softmax, so their finite
+  // stand-in values get zero weight.  PF register sets keep PF tiles in flight.
   constexpr int OCT = D / 8;
   constexpr int K_TOTAL = kKeyTile * OCT;                          // 16-byte K units per tile
-  constexpr int V_TOTAL = (kKeyTile / 4) * OCT;                    // 4-key V units per tile
-  constexpr int K_UNITS = (K_TOTAL + kThreads - 1) / kThreads;     // per thread
-  constexpr int V_UNITS = (V_TOTAL + kThreads - 1) / kThreads;
-  bf16x8 kreg[K_UNITS];
-  bf16x8 vreg[V_UNITS][4];
+  constexpr int K_UNITS = K_TOTAL / kThreads;                      // per thread
+  constexpr int VK = kKeyTile * OCT / kThreads;                    // keys per V unit
+  static_assert(K_TOTAL % kThreads == 0 && VK >= 1 && VK <= 4, "tile split");
+  const int klast = k_end - 1;
 
-  auto load_tile = [&](int kt0) {
+  auto load_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0) {
 #pragma unroll
     for (int u = 0; u < K_UNITS; ++u) {
       const int unit = tid + u * kThreads;
       const int key = unit / OCT, oc = unit - (unit / OCT) * OCT;
-      const int kidx = kt0 + key;
-      kreg[u] = (unit < K_TOTAL && kidx < k_end)
-                    ? *reinterpret_cast<const bf16x8*>(kbase + (size_t)kidx * D + oc * 8)
-                    : bf16x8{};
+      const int kidx = min(kt0 + key, klast);
+      kr[u] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kidx * D + oc * 8);
     }
+    const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
 #pragma unroll
-    for (int u = 0; u < V_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int kq = unit / OCT, oc = unit - (unit / OCT) * OCT;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kidx = kt0 + 4 * kq + j;
-        vreg[u][j] = (unit < V_TOTAL && kidx < k_end)
-                         ? *reinterpret_cast<const bf16x8*>(vbase + (size_t)kidx * D + oc * 8)
-                         : bf16x8{};
-      }
+    for (int j = 0; j < VK; ++j) {
+      const int kidx = min(kt0 + VK * kq + j, klast);
+      vr[j] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kidx * D + oc * 8);
     }
   };
-  auto store_tile = [&](int stage) {
+  auto store_tile = [&](const bf16x8 (&kr)[K_UNITS], const bf16x8 (&vr)[VK], int stage) {
     bf16_t* sk = smem + stage * Lds<D>::kStage;
     bf16_t* sv = sk + Lds<D>::kStageK;
 #pragma unroll
     for (int u = 0; u < K_UNITS; ++u) {
       const int unit = tid + u * kThreads;
-      if (unit >= K_TOTAL) continue;
       const int key = unit / OCT, oc = unit - (unit / OCT) * OCT;
-      *reinterpret_cast<bf16x8*>(sk + key * Lds<D>::kPitchK + oc * 8) = kreg[u];
+      *reinterpret_cast<bf16x8*>(sk + key * Lds<D>::kPitchK + oc * 8) = kr[u];
     }
+    const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
 #pragma unroll
-    for (int u = 0; u < V_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      if (unit >= V_TOTAL) continue;
-      const int kq = unit / OCT, oc = unit - (unit / OCT) * OCT;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 w{vreg[u][0][e], vreg[u][1][e], vreg[u][2][e], vreg[u][3][e]};
-        *reinterpret_cast<bf16x4*>(sv + (oc * 8 + e) * Lds<D>::kPitchV + 4 * kq) = w;
+    for (int e = 0; e < 8; ++e) {
+      bf16_t* dst = sv + (oc * 8 + e) * Lds<D>::kPitchV + VK * kq;
+      if constexpr (VK == 4) {
+        *reinterpret_cast<bf16x4*>(dst) = bf16x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
+      } else if constexpr (VK == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<bf16x2*>(dst) = bf16x2{vr[0][e], vr[1][e]};
+      } else {
+        *dst = vr[0][e];
       }
     }
   };
 
-  const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
-  load_tile(k_begin);
-  store_tile(0);
-  __syncthreads();
+  const float c = a.scale_log2;
+  const int wkey0 = kg * KEYS_W;  // first key of this wave inside a tile
 
-  for (int it = 0; it < n_tiles; ++it) {
-    const int kt0 = k_begin + it * kKeyTile;
-    const bool more = it + 1 < n_tiles;
-    if (more) load_tile(kt0 + kKeyTile);
-    const bf16_t* sk = smem + (it & 1) * Lds<D>::kStage;
+  // One 64-key tile from LDS stage `stage` (first key kt0).  Each 32-key chunk of
+  // this wave's keys: S^T = K Q^T (two 16-key sub-tiles), online softmax, then
+  // O^T += V^T P^T with the chunk as one 32-key k-step.
+  auto compute_tile = [&](int stage, int kt0) {
+    const bf16_t* sk = smem + stage * Lds<D>::kStage;
     const bf16_t* sv = sk + Lds<D>::kStageK;
-    const int wkey0 = kg * KEYS_W;  // first key of this wave inside the tile
     const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
-
-    // S^T = K Q^T for this wave's SUB sub-tiles
-    f32x4 sacc[QT][SUB];
-#pragma unroll
-    for (int st = 0; st < SUB; ++st) {
-      bf16x8 kf[KSTEPS];
-      const bf16_t* krow = sk + (wkey0 + 16 * st + l16) * Lds<D>::kPitchK + 8 * lg;
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
-#pragma unroll
-      for (int i = 0; i < QT; ++i) {
-        f32x4 c{0.f, 0.f, 0.f, 0.f};
-        if (qt_on[i]) {
-#pragma unroll
-          for (int s = 0; s < KSTEPS; ++s) c = mfma16x16x32(kf[s], qf[i][s], c);
-        }
-        sacc[i][st] = c;
-      }
-    }
-
-    // online softmax (exp2 form); lane owns query l16, keys 16*st + 4*lg + e
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-      if (!qt_on[i]) continue;
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int st = 0; st < SUB; ++st) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float s = sacc[i][st][e] * scale_log2;
-          if (need_mask) {
-            const int key = kt0 + wkey0 + 16 * st + 4 * lg + e;
-            bool vis = key < k_end;
-            if (vis && key >= ctx) {
-              const int a = key - ctx;
-              const uint64_t w = a < 64 ? mask0[i] : mask1[i];
-              vis = (w >> (a & 63)) & 1ull;
-            }
-            if (!vis) s = -INFINITY;
-          }
-          sacc[i][st][e] = s;
-          tmax = fmaxf(tmax, s);
-        }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, kWave));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-      const float m_new = fmaxf(m_run[i], tmax);
-      float alpha = 1.0f;
-      if (m_new != -INFINITY) {
-        alpha = __builtin_amdgcn_exp2f(m_run[i] - m_new);
-      }
-      float psum = 0.0f;
-#pragma unroll
-      for (int st = 0; st < SUB; ++st) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float pv = m_new == -INFINITY ? 0.0f
-                                              : __builtin_amdgcn_exp2f(sacc[i][st][e] - m_new);
-          sacc[i][st][e] = pv;
-          psum += pv;
-        }
-      }
-      m_run[i] = m_new;
-      l_run[i] = l_run[i] * alpha + psum;
-#pragma unroll
-      for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
-    }
-
-    // O^T += V^T P^T: one 32-key k-step pairs sub-tiles (2j, 2j+1)
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
+      const int ck0 = wkey0 + 32 * j;  // first key of the chunk inside the tile
+      f32x4 sacc[QT][2];
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        bf16x8 kf[KSTEPS];
+        const bf16_t* krow = sk + (ck0 + 16 * st + l16) * Lds<D>::kPitchK + 8 * lg;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+          f32x4 cc{0.f, 0.f, 0.f, 0.f};
+          if (qt_on[i]) {
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) cc = mfma16x16x32(kf[s], qf[i][s], cc);
+          }
+          sacc[i][st] = cc;
+        }
+      }
+
+      // keys past the range or outside the node's ancestor set score -inf
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int key = kt0 + ck0 + 16 * st + 4 * lg + e;
+              const int aa = key - ctx;
+              const uint64_t w = aa < 64 ? mask0[i] : mask1[i];
+              const bool tree_vis = ((w >> (aa & 63)) & 1ull) != 0ull;
+              const bool vis = key < k_end && (aa < 0 || tree_vis);
+              sacc[i][st][e] = vis ? sacc[i][st][e] : -INFINITY;
+            }
+          }
+        }
+      }
+
+      // online softmax in exp2 form; lane owns query l16, keys ck0 + 16*st + 4*lg + e
       bf16x8 pf[QT];
 #pragma unroll
       for (int i = 0; i < QT; ++i) {
+        if (!qt_on[i]) continue;
+        float lmax = fmaxf(fmaxf(fmaxf(sacc[i][0][0], sacc[i][0][1]),
+                                 fmaxf(sacc[i][0][2], sacc[i][0][3])),
+                           fmaxf(fmaxf(sacc[i][1][0], sacc[i][1][1]),
+                                 fmaxf(sacc[i][1][2], sacc[i][1][3])));
+        lmax *= c;
+        // the row maximum moves only when some lane outgrew it by 2^kRescale;
+        // then the 4 lane groups holding the row agree on the new maximum
+        if (__builtin_amdgcn_ballot_w64(lmax > m_run[i] + kRescale) != 0ull) {
+          float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
+          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+          const float m_new = fmaxf(m_run[i], tmax);
+          const float alpha =
+              (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+          l_run[i] *= alpha;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pf[i][e] = (bf16_t)sacc[i][2 * j][e];
-          pf[i][4 + e] = (bf16_t)sacc[i][2 * j + 1][e];
+          for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
+          m_run[i] = m_new;
         }
+        const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
+        float psum = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i][st][e], c, nmu));
+            pf[i][4 * st + e] = (bf16_t)pv;
+            psum += pv;
+          }
+        }
+        l_run[i] += psum;
       }
-      const int key_a = wkey0 + 32 * j + 4 * lg;  // keys of sub-tile 2j owned by this lane group
+
+      // O^T += V^T P^T over the chunk's 32 keys
+      const int key_a = ck0 + 4 * lg;  // keys of the first sub-tile owned by this lane group
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
@@ -385,9 +414,48 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
           if (qt_on[i]) acc[i][d] = mfma16x16x32(vf, pf[i], acc[i][d]);
       }
     }
+  };
 
-    if (more) store_tile((it + 1) & 1);
-    __syncthreads();
+  // ---------------------------------------------------------------- key loop
+  // LDS double buffer; PF tiles of global loads in flight.  The barrier waits
+  // for this wave's LDS traffic only, so prefetched global loads stay in flight.
+  const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
+  bf16x8 kA[K_UNITS], vA[VK];
+  load_tile(kA, vA, k_begin);
+  if constexpr (PF == 1) {
+    store_tile(kA, vA, 0);
+    lds_barrier();
+#pragma unroll 1
+    for (int it = 0; it < n_tiles; ++it) {
+      const int kt0 = k_begin + it * kKeyTile;
+      const bool more = it + 1 < n_tiles;
+      if (more) load_tile(kA, vA, kt0 + kKeyTile);
+      compute_tile(it & 1, kt0);
+      if (more) store_tile(kA, vA, (it + 1) & 1);
+      lds_barrier();
+    }
+  } else {
+    // Two register sets (A: even tiles, B: odd tiles) alternate over the two
+    // LDS stages.  Loads are unconditional (indices clamp to the last key, so
+    // loads past the end fetch a resident row) and the loop body is straight
+    // line, so the loads of the next two tiles stay in flight across barriers.
+    bf16x8 kB[K_UNITS], vB[VK];
+    load_tile(kB, vB, k_begin + kKeyTile);
+    store_tile(kA, vA, 0);
+    lds_barrier();
+    const int n_pairs = (n_tiles + 1) >> 1;
+#pragma unroll 1
+    for (int it = 0; it < n_pairs; ++it) {
+      const int kt0 = k_begin + 2 * it * kKeyTile;  // tile 2it in stage 0, 2it+1 in B
+      load_tile(kA, vA, kt0 + 2 * kKeyTile);
+      compute_tile(0, kt0);
+      store_tile(kB, vB, 1);
+      lds_barrier();
+      load_tile(kB, vB, kt0 + 3 * kKeyTile);
+      if (2 * it + 1 < n_tiles) compute_tile(1, kt0 + kKeyTile);
+      store_tile(kA, vA, 0);
+      lds_barrier();
+    }
   }
 
   // ---------------------------------------------------------------- combine lanes
@@ -403,6 +471,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
     float* xs = reinterpret_cast<float*>(smem_raw);  // LDS reused after the loop
     // per row group: QT * (DT*4*64 acc floats + 64 m + 64 l)
     constexpr int PER_QT = DT * 4 * 64 + 128;
+    static_assert(RG * QT * PER_QT * 4 <= Lds<D>::kBytes, "key-group exchange fits in LDS");
     float* mine = xs + rg * QT * PER_QT;
     if (kg == 1) {
 #pragma unroll
@@ -429,7 +498,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
 #pragma unroll
       for (int d = 0; d < DT; ++d)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][d][e] = acc[i][d][e] * a1 + p[(d * 4 + e) * 64 + lane] * a2;
+        for (int e = 0; e < 4; ++e)
+          acc[i][d][e] = acc[i][d][e] * a1 + p[(d * 4 + e) * 64 + lane] * a2;
       m_run[i] = m_new;
       l_run[i] = l_run[i] * a1 + l2 * a2;
     }
@@ -443,9 +513,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
     if (qt_idx[i] * 16 >= M_cap || r >= M_cap) continue;
     const int t = r / G;
     const int gq = r - t * G;
+    const bool live = qt_on[i] && r < rows_valid;
     if (n_splits == 1) {
-      bf16_t* orow = out + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
-      const bool live = qt_on[i] && r < rows_valid;
+      bf16_t* orow = a.out + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
       const float inv = (live && l_run[i] > 0.f) ? 1.0f / l_run[i] : 0.0f;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
@@ -456,63 +526,71 @@ __global__ __launch_bounds__(kThreads, 2) void k_attn_bf16(
       }
     } else {
       const size_t ubase = (size_t)kv_unit * M_cap;
-      const bool live = qt_on[i] && r < rows_valid;
-      float* po = part_o + (ubase + r) * D;
+      float* po = a.part_o + (ubase + r) * D;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         f32x4 o = live ? acc[i][d] : f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(po + 16 * d + 4 * lg) = o;
       }
       if (lg == 0) {
-        part_m[ubase + r] = live ? m_run[i] : -INFINITY;
-        part_l[ubase + r] = live ? l_run[i] : 0.0f;
+        a.part_m[ubase + r] = live ? m_run[i] : -INFINITY;
+        a.part_l[ubase + r] = live ? l_run[i] : 0.0f;
       }
     }
   }
 }
 
-// Combine the per-split partials of one (b, kv head, row) and write bf16 rows.
-__global__ __launch_bounds__(256) void k_attn_merge(int B, int T_cap, int H, int Hkv, int D,
-                                                    int cache_cap, int max_ctx, int n_splits,
+// Combine the per-split partials of one (b, kv head) and write bf16 rows.  A
+// thread owns one row and 4 output dims; the loads of all splits are issued
+// together (unrolled up to MAXS) so the merge runs at memory speed.
+template <int D, int MAXS>
+__global__ __launch_bounds__(256) void k_attn_merge(int T_cap, int H, int Hkv, int cache_cap,
+                                                    int max_ctx, int n_splits,
                                                     const int32_t* __restrict__ ctx_len,
                                                     const int32_t* __restrict__ n_nodes,
                                                     const float* __restrict__ part_o,
                                                     const float* __restrict__ part_m,
                                                     const float* __restrict__ part_l,
                                                     bf16_t* __restrict__ out) {
+  constexpr int TPR = D / 4;          // threads per row
+  constexpr int RPB = 256 / TPR;      // rows per block
   const int G = H / Hkv;
   const int M_cap = G * T_cap;
   const int bh = blockIdx.y;
   const int b = bh / Hkv, g_kv = bh - (bh / Hkv) * Hkv;
+  const int r = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int d0 = 4 * (threadIdx.x % TPR);
+  if (r >= M_cap) return;
   const int ctx = ctx_len[b], T = n_nodes[b];
   const bool bad = T < 1 || T > T_cap || ctx < 0 || ctx > max_ctx || ctx + T > cache_cap;
   const int rows_valid = bad ? 0 : G * T;
-  const int per_block = 256 / D > 0 ? 256 / D : 1;
-  const int r = blockIdx.x * per_block + threadIdx.x / D;
-  const int d = threadIdx.x % D;
-  if (r >= M_cap || threadIdx.x >= per_block * D) return;
   const int t = r / G, gq = r - t * G;
-  float val = 0.0f;
+  f32x4 o{0.f, 0.f, 0.f, 0.f};
   if (r < rows_valid) {
+    float ms[MAXS];
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) {
-      const size_t u = (size_t)bh * n_splits + s;
-      M = fmaxf(M, part_m[u * M_cap + r]);
+#pragma unroll
+    for (int s = 0; s < MAXS; ++s) {
+      ms[s] = s < n_splits ? part_m[((size_t)bh * n_splits + s) * M_cap + r] : -INFINITY;
+      M = fmaxf(M, ms[s]);
     }
-    float L = 0.0f, O = 0.0f;
+    float L = 0.0f;
     if (M != -INFINITY) {
-      for (int s = 0; s < n_splits; ++s) {
+#pragma unroll
+      for (int s = 0; s < MAXS; ++s) {
+        if (ms[s] == -INFINITY) continue;
         const size_t u = (size_t)bh * n_splits + s;
-        const float ms = part_m[u * M_cap + r];
-        if (ms == -INFINITY) continue;
-        const float w = __builtin_amdgcn_exp2f(ms - M);
+        const float w = __builtin_amdgcn_exp2f(ms[s] - M);
         L += part_l[u * M_cap + r] * w;
-        O += part_o[(u * M_cap + r) * D + d] * w;
+        const f32x4 po = *reinterpret_cast<const f32x4*>(part_o + (u * M_cap + r) * D + d0);
+        o += po * w;
       }
     }
-    val = L > 0.0f ? O / L : 0.0f;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    o *= inv;
   }
-  out[(((size_t)b * T_cap + t) * H + g_kv * G + gq) * D + d] = (bf16_t)val;
+  bf16x4 ob{(bf16_t)o[0], (bf16_t)o[1], (bf16_t)o[2], (bf16_t)o[3]};
+  *reinterpret_cast<bf16x4*>(out + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D + d0) = ob;
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -559,8 +637,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
   float m = -INFINITY, l = 0.0f;
   for (int j = 0; j < ctx + T; ++j) {
     if (j >= ctx) {
-      const int a = j - ctx;
-      if (!((arow[a >> 6] >> (a & 63)) & 1ull)) continue;
+      const int aa = j - ctx;
+      if (!((arow[aa >> 6] >> (aa & 63)) & 1ull)) continue;
     }
     float part = 0.0f;
 #pragma unroll
@@ -587,38 +665,99 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
   }
 }
 
-template <int D, int QT, int KG>
-int launch_bf16(const AttnPlan& p, int B, int T_cap, int H, int Hkv, int cache_cap, int max_ctx,
-                const void* q, const void* k, const void* v, const int32_t* ctx_len,
-                const int32_t* n_nodes, const uint64_t* anc, float scale_log2, void* out,
-                float* po, float* pm, float* pl, int32_t* status, hipStream_t s) {
-  auto kern = k_attn_bf16<D, QT, KG>;
+// ------------------------------------------------------------------ launchers
+
+template <int D, int NW, int QT, int KG, int PF>
+int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
+  auto kern = k_attn_bf16<D, NW, QT, KG, PF>;
   const int lds = Lds<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                      hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  hipLaunchKernelGGL(kern, dim3(p.n_slots), dim3(kThreads), lds, s, B, T_cap, H, Hkv, cache_cap,
-                     max_ctx, p.n_splits, p.tiles_per_split, p.n_kv, p.n_mt,
-                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k),
-                     static_cast<const bf16_t*>(v), ctx_len, n_nodes, anc, scale_log2,
-                     static_cast<bf16_t*>(out), po, pm, pl, status);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipLaunchKernelGGL(kern, dim3(p.n_slots), dim3(NW * 64), lds, s, args);
   return launch_status();
 }
 
 template <int D>
-int dispatch_bf16(const AttnPlan& p, int B, int T_cap, int H, int Hkv, int cache_cap,
-                  int max_ctx, const void* q, const void* k, const void* v,
-                  const int32_t* ctx_len, const int32_t* n_nodes, const uint64_t* anc,
-                  float scale_log2, void* out, float* po, float* pm, float* pl, int32_t* status,
-                  hipStream_t s) {
-#define SPEC_ATTN_CASE(QT_, KG_)                                                              \
-  if (p.QT == QT_ && p.KG == KG_)                                                             \
-    return launch_bf16<D, QT_, KG_>(p, B, T_cap, H, Hkv, cache_cap, max_ctx, q, k, v, ctx_len, \
-                                    n_nodes, anc, scale_log2, out, po, pm, pl, status, s);
-  SPEC_ATTN_CASE(1, 2)
-  SPEC_ATTN_CASE(2, 2)
-  SPEC_ATTN_CASE(2, 1)
+int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
+#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_)                            \
+  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_)       \
+    return launch_main<D, NW_, QT_, KG_, PF_>(p, args, s);
+  SPEC_ATTN_CASE(4, 1, 2, 1)
+  SPEC_ATTN_CASE(4, 2, 2, 1)
+  SPEC_ATTN_CASE(4, 1, 1, 1)
+  SPEC_ATTN_CASE(4, 2, 1, 1)
+  SPEC_ATTN_CASE(8, 1, 2, 1)
+  SPEC_ATTN_CASE(8, 1, 1, 1)
+  SPEC_ATTN_CASE(8, 2, 1, 1)
+  SPEC_ATTN_CASE(4, 1, 2, 2)
+  SPEC_ATTN_CASE(4, 2, 2, 2)
+  SPEC_ATTN_CASE(4, 1, 1, 2)
+  SPEC_ATTN_CASE(4, 2, 1, 2)
+  SPEC_ATTN_CASE(8, 1, 2, 2)
+  SPEC_ATTN_CASE(8, 1, 1, 2)
+  SPEC_ATTN_CASE(8, 2, 1, 2)
 #undef SPEC_ATTN_CASE
   return SPEC_ERR_UNSUPPORTED;
+}
+
+template <int D>
+int launch_merge(const AttnPlan& p, const AttnArgs& a, hipStream_t s) {
+  constexpr int RPB = 256 / (D / 4);
+  const int G = a.H / a.Hkv;
+  dim3 grid((G * a.T_cap + RPB - 1) / RPB, a.B * a.Hkv);
+#define SPEC_MERGE_CASE(MAXS_)                                                                  \
+  if (p.n_splits <= MAXS_) {                                                                   \
+    hipLaunchKernelGGL((k_attn_merge<D, MAXS_>), grid, dim3(256), 0, s, a.T_cap, a.H, a.Hkv,   \
+                       a.cache_cap, a.max_ctx, p.n_splits, a.ctx_len, a.n_nodes, a.part_o,     \
+                       a.part_m, a.part_l, a.out);                                             \
+    return launch_status();                                                                    \
+  }
+  SPEC_MERGE_CASE(4)
+  SPEC_MERGE_CASE(8)
+  SPEC_MERGE_CASE(16)
+  SPEC_MERGE_CASE(32)
+#undef SPEC_MERGE_CASE
+  return SPEC_ERR_UNSUPPORTED;
+}
+
+// Validated launch of the bf16 path with a given plan (ws already checked).
+int run_bf16(const AttnPlan& p, int B, int T_cap, int H, int Hkv, int D, int cache_cap,
+             int max_ctx, const void* q, const void* k_cache, const void* v_cache,
+             const int32_t* ctx_len, const int32_t* n_nodes, const uint64_t* anc, float scale,
+             void* out, void* ws, int32_t* status, hipStream_t s) {
+  AttnArgs a{};
+  a.B = B;
+  a.T_cap = T_cap;
+  a.H = H;
+  a.Hkv = Hkv;
+  a.cache_cap = cache_cap;
+  a.max_ctx = max_ctx;
+  a.n_splits = p.n_splits;
+  a.tiles_per_split = p.tiles_per_split;
+  a.n_kv = p.n_kv;
+  a.n_mt = p.n_mt;
+  a.scale_log2 = scale * kLog2e;
+  a.q = static_cast<const bf16_t*>(q);
+  a.kc = static_cast<const bf16_t*>(k_cache);
+  a.vc = static_cast<const bf16_t*>(v_cache);
+  a.ctx_len = ctx_len;
+  a.n_nodes = n_nodes;
+  a.anc = anc;
+  a.out = static_cast<bf16_t*>(out);
+  a.status = status;
+  if (p.n_splits > 1) {
+    const size_t rows = (size_t)(H / Hkv) * T_cap;
+    const size_t units = (size_t)B * Hkv * p.n_splits;
+    char* w = static_cast<char*>(ws);
+    a.part_o = reinterpret_cast<float*>(w);
+    w += round_up(units * rows * D * sizeof(float), 256);
+    a.part_m = reinterpret_cast<float*>(w);
+    w += round_up(units * rows * sizeof(float), 256);
+    a.part_l = reinterpret_cast<float*>(w);
+  }
+  int rc = D == 128 ? dispatch_main<128>(p, a, s) : dispatch_main<64>(p, a, s);
+  if (rc != SPEC_OK || p.n_splits <= 1) return rc;
+  return D == 128 ? launch_merge<128>(p, a, s) : launch_merge<64>(p, a, s);
 }
 
 }  // namespace
@@ -664,31 +803,7 @@ extern "C" int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int
     return SPEC_ERR_INVALID;
   const AttnPlan p = make_plan(B, T_cap, H, Hkv, max_ctx);
   const size_t need = partial_bytes(p, B, T_cap, H, Hkv, D);
-  float *po = nullptr, *pm = nullptr, *pl = nullptr;
-  if (need) {
-    if (!ws || ws_bytes < need || !aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
-    const size_t rows = (size_t)(H / Hkv) * T_cap;
-    const size_t units = (size_t)B * Hkv * p.n_splits;
-    char* w = static_cast<char*>(ws);
-    po = reinterpret_cast<float*>(w);
-    w += round_up(units * rows * D * sizeof(float), 256);
-    pm = reinterpret_cast<float*>(w);
-    w += round_up(units * rows * sizeof(float), 256);
-    pl = reinterpret_cast<float*>(w);
-  }
-  const float scale_log2 = scale * kLog2e;
-  int rc = D == 128 ? dispatch_bf16<128>(p, B, T_cap, H, Hkv, cache_cap, max_ctx, q, k_cache,
-                                         v_cache, ctx_len, n_nodes, anc, scale_log2, out, po, pm,
-                                         pl, status, s)
-                    : dispatch_bf16<64>(p, B, T_cap, H, Hkv, cache_cap, max_ctx, q, k_cache,
-                                        v_cache, ctx_len, n_nodes, anc, scale_log2, out, po, pm,
-                                        pl, status, s);
-  if (rc != SPEC_OK || p.n_splits <= 1) return rc;
-  const int G = H / Hkv;
-  const int per_block = 256 / D;
-  dim3 grid((G * T_cap + per_block - 1) / per_block, B * Hkv);
-  hipLaunchKernelGGL(k_attn_merge, grid, dim3(256), 0, s, B, T_cap, H, Hkv, D, cache_cap,
-                     max_ctx, p.n_splits, ctx_len, n_nodes, po, pm, pl,
-                     static_cast<bf16_t*>(out));
-  return launch_status();
+  if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return SPEC_ERR_WORKSPACE;
+  return run_bf16(p, B, T_cap, H, Hkv, D, cache_cap, max_ctx, q, k_cache, v_cache, ctx_len,
+                  n_nodes, anc, scale, out, ws, status, s);
 }

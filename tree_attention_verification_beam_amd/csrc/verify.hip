@@ -44,12 +44,28 @@ struct Partial {
   int arg;   // lowest index attaining m
 };
 
+// Partials cross workgroups through the device-coherent level (two 64-bit words).
+__device__ inline void store_partial(Partial* p, double S, float m, int arg) {
+  uint64_t* w = reinterpret_cast<uint64_t*>(p);
+  store_coherent(w, __double_as_longlong(S));
+  store_coherent(w + 1, (uint64_t)__float_as_uint(m) | ((uint64_t)(uint32_t)arg << 32));
+}
+__device__ inline Partial load_partial(const Partial* p) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
+  const uint64_t a = load_coherent(w), b = load_coherent(w + 1);
+  Partial r;
+  r.S = __longlong_as_double((long long)a);
+  r.m = __uint_as_float((uint32_t)b);
+  r.arg = (int)(uint32_t)(b >> 32);
+  return r;
+}
+
 struct VerifyPlan {
   int ept;       // floats per thread in k_vstats
   int chunk;     // floats per chunk
   int n_chunks;  // chunks per row
   long n_units;  // rows: B*T_cap target rows, then B*R draft rows
-  size_t off_part, off_need, off_bad, off_sync, total;
+  size_t off_part, off_row, off_cnt, off_need, off_bad, off_sync, total;
 };
 
 VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
@@ -64,6 +80,10 @@ VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
   size_t off = 0;
   p.off_part = off;
   off += round_up((size_t)p.n_units * p.n_chunks * sizeof(Partial), 256);
+  p.off_row = off;
+  off += round_up((size_t)p.n_units * sizeof(Partial), 256);
+  p.off_cnt = off;
+  off += round_up((size_t)p.n_units * sizeof(int32_t), 256);
   p.off_need = off;
   off += round_up((size_t)B * (Rr > 0 ? Rr : 1) * sizeof(int32_t), 256);
   p.off_bad = off;
@@ -132,7 +152,7 @@ __global__ __launch_bounds__(SPEC_MAX_TREE) void k_vprep(
     const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
     const int32_t* __restrict__ depth, const int32_t* __restrict__ dft_row,
     int32_t* __restrict__ need, int32_t* __restrict__ seq_bad, unsigned char* __restrict__ sync,
-    int32_t* __restrict__ status) {
+    int32_t* __restrict__ cnt, int B, int32_t* __restrict__ status) {
   __shared__ int s_has_child[SPEC_MAX_TREE];
   __shared__ int s_bad;
   const int b = blockIdx.x, t = threadIdx.x;
@@ -140,7 +160,11 @@ __global__ __launch_bounds__(SPEC_MAX_TREE) void k_vprep(
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
   if (t == 0) s_bad = 0;
   s_has_child[t] = 0;
-  for (int r = t; r < Rr; r += SPEC_MAX_TREE) need[(size_t)b * Rr + r] = 0;
+  for (int r = t; r < Rr; r += SPEC_MAX_TREE) {
+    need[(size_t)b * Rr + r] = 0;
+    cnt[(size_t)B * T_cap + (size_t)b * Rr + r] = 0;
+  }
+  for (int r = t; r < T_cap; r += SPEC_MAX_TREE) cnt[(size_t)b * T_cap + r] = 0;
   __syncthreads();
   if (T < 1 || T > T_cap) {
     if (t == 0) {
@@ -183,7 +207,9 @@ template <int EPT, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void k_vstats(
     int B, int T_cap, int V, int Rr, int n_chunks, const float* __restrict__ tgt,
     const float* __restrict__ dft, const int32_t* __restrict__ n_nodes,
-    const int32_t* __restrict__ need, Partial* __restrict__ part) {
+    const int32_t* __restrict__ need, Partial* __restrict__ part, Partial* __restrict__ rows,
+    int32_t* __restrict__ cnt) {
+  __shared__ int s_last;
   __shared__ float s_m[kStatThreads / 64];
   __shared__ int s_a[kStatThreads / 64];
   __shared__ double s_s[kStatThreads / 64];
@@ -261,11 +287,40 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
   if (tid == 0) {
     double tot = 0.0;
     for (int w = 0; w < kStatThreads / 64; ++w) tot += s_s[w];
-    Partial p;
-    p.S = tot;
-    p.m = m;
-    p.arg = a;
-    part[unit * n_chunks + c] = p;
+    // publish the chunk's partial at the coherent level, then count it; the
+    // workgroup that completes a row's last chunk merges the row
+    store_partial(part + unit * n_chunks + c, tot, m, a);
+    wait_stores_done();
+    s_last = atomicAdd(cnt + unit, 1) == n_chunks - 1;
+  }
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+  // one wave: lanes over the chunks (increasing index within a lane), then the
+  // wave combines (max, lowest argmax, sum rescaled to the row maximum) in fp64
+  float mr = -INFINITY;
+  int ar = 0x7fffffff;
+  double Sr = 0.0;
+  for (int cc = lane; cc < n_chunks; cc += 64) {
+    const Partial q = load_partial(part + unit * n_chunks + cc);
+    if (q.m > mr) {
+      Sr = (mr == -INFINITY ? 0.0 : Sr * exp((double)mr - (double)q.m)) + q.S;
+      mr = q.m;
+      ar = q.arg;
+    } else if (q.m != -INFINITY) {
+      Sr += q.S * exp((double)q.m - (double)mr);
+    }
+  }
+  float mw = mr;
+  int aw = ar;
+  wave_argmax(mw, aw);
+  const double Sw = wave_sum_f64(mr == -INFINITY ? 0.0 : Sr * exp((double)mr - (double)mw));
+  if (lane == 0) {
+    Partial r;
+    r.S = Sw;
+    r.m = mw;
+    r.arg = aw;
+    rows[unit] = r;
+    cnt[unit] = 0;
   }
 }
 
@@ -282,7 +337,7 @@ struct SelArgs {
   const int32_t* depth;
   const float* u_node;
   const float* u_final;
-  const Partial* part;
+  const Partial* rows;
   const int32_t* seq_bad;
   unsigned char* sync;
   int32_t* acc_len;
@@ -346,12 +401,14 @@ struct SeqSync {
     }
     __syncthreads();
     if (threadIdx.x == 0) {
+      // slots are written and read at the coherent level; the count follows
+      // the completed slot stores
       publish(a, b);
-      __atomic_thread_fence(__ATOMIC_RELEASE);
-      __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      wait_stores_done();
+      __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int target = P * (rounds + 1);
       int spins = 0;
-      while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
         __builtin_amdgcn_s_sleep(1);
         if (++spins > (1 << 24)) {
           raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
@@ -541,20 +598,6 @@ __device__ bool pass_draw(const RowPair& rp, int k, const double* invN, double u
   return true;
 }
 
-// merge the chunk partials of one row: max, lowest argmax, sum rescaled (fp64)
-__device__ inline void merge_row(const Partial* p, int n_chunks, float& m, int& arg, double& S) {
-  m = -INFINITY;
-  arg = 0;
-  for (int c = 0; c < n_chunks; ++c)
-    if (p[c].m > m) {
-      m = p[c].m;
-      arg = p[c].arg;
-    }
-  S = 0.0;
-  for (int c = 0; c < n_chunks; ++c)
-    if (p[c].m != -INFINITY) S += p[c].S * exp((double)p[c].m - (double)m);
-}
-
 template <int MODE>
 __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   __shared__ SelShared sh;
@@ -591,30 +634,20 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   }
   __syncthreads();
   for (int t = tid + 1; t < T; t += kSelThreads) atomicAdd(&sh.nch[sh.par[t]], 1);
+  __syncthreads();
+  // row statistics, merged per row by the vocabulary pass
   for (int t = tid; t < T; t += kSelThreads) {
-    float m;
-    int arg;
-    double S;
-    merge_row(A.part + (nb + t) * A.n_chunks, A.n_chunks, m, arg, S);
-    sh.m_p[t] = m;
-    sh.arg_p[t] = arg;
-    sh.S_p[t] = S;
+    const Partial r = A.rows[nb + t];
+    sh.m_p[t] = r.m;
+    sh.arg_p[t] = r.arg;
+    sh.S_p[t] = r.S;
+    if (MODE != SPEC_GREEDY && sh.nch[t] > 0) {
+      const Partial rq = A.rows[(size_t)A.B * T_cap + (size_t)b * A.Rr + A.dft_row[nb + t]];
+      sh.m_q[t] = rq.m;
+      sh.S_q[t] = rq.S;
+    }
   }
   __syncthreads();
-  if (MODE != SPEC_GREEDY) {
-    for (int t = tid; t < T; t += kSelThreads) {
-      if (sh.nch[t] == 0) continue;
-      const int r = A.dft_row[nb + t];
-      float m;
-      int arg;
-      double S;
-      merge_row(A.part + ((size_t)A.B * T_cap + (size_t)b * A.Rr + r) * A.n_chunks, A.n_chunks, m,
-                arg, S);
-      sh.m_q[t] = m;
-      sh.S_q[t] = S;
-    }
-    __syncthreads();
-  }
   // p and q of every node's own token under its parent (fp64 exp, merged sums)
   for (int t = tid + 1; t < T; t += kSelThreads) {
     const int s = sh.par[t], x = sh.tok[t];
@@ -819,14 +852,14 @@ int choose_p(int mode, int B, int V) {
 template <int EPT>
 void launch_stats(const VerifyPlan& pl, bool vec, int B, int T_cap, int V, int Rr,
                   const float* tgt, const float* dft, const int32_t* n_nodes, const int32_t* need,
-                  Partial* part, hipStream_t s) {
+                  Partial* part, Partial* rows, int32_t* cnt, hipStream_t s) {
   const dim3 grid((unsigned)(pl.n_units * pl.n_chunks));
   if (vec)
     hipLaunchKernelGGL((k_vstats<EPT, true>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
-                       pl.n_chunks, tgt, dft, n_nodes, need, part);
+                       pl.n_chunks, tgt, dft, n_nodes, need, part, rows, cnt);
   else
     hipLaunchKernelGGL((k_vstats<EPT, false>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
-                       pl.n_chunks, tgt, dft, n_nodes, need, part);
+                       pl.n_chunks, tgt, dft, n_nodes, need, part, rows, cnt);
 }
 
 }  // namespace
@@ -862,18 +895,20 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   char* w = static_cast<char*>(ws);
   Partial* part = reinterpret_cast<Partial*>(w + pl.off_part);
   int32_t* need = reinterpret_cast<int32_t*>(w + pl.off_need);
+  Partial* rows = reinterpret_cast<Partial*>(w + pl.off_row);
+  int32_t* cnt = reinterpret_cast<int32_t*>(w + pl.off_cnt);
   int32_t* seq_bad = reinterpret_cast<int32_t*>(w + pl.off_bad);
   unsigned char* sync = reinterpret_cast<unsigned char*>(w + pl.off_sync);
   hipStream_t s = as_stream(stream);
 
   hipLaunchKernelGGL(k_vprep, dim3(B), dim3(SPEC_MAX_TREE), 0, s, mode, T_cap, V, Rr, n_nodes,
-                     parent, token, depth, dft_row, need, seq_bad, sync, status);
+                     parent, token, depth, dft_row, need, seq_bad, sync, cnt, B, status);
   const bool vec = (V % 4 == 0) && aligned(tgt, 16) && (Rr == 0 || aligned(dft, 16));
   switch (pl.ept) {
-    case 32: launch_stats<32>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
-    case 16: launch_stats<16>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
-    case 8: launch_stats<8>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
-    default: launch_stats<4>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, s); break;
+    case 32: launch_stats<32>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
+    case 16: launch_stats<16>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
+    case 8: launch_stats<8>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
+    default: launch_stats<4>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
   }
   int rc = launch_status();
   if (rc != SPEC_OK) return rc;
@@ -894,7 +929,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   A.depth = depth;
   A.u_node = u_node;
   A.u_final = u_final;
-  A.part = part;
+  A.rows = rows;
   A.seq_bad = seq_bad;
   A.sync = sync;
   A.acc_len = acc_len;
