@@ -64,3 +64,14 @@ def test_validation_rejects_before_launch(lib):
     assert cdll.spec_tree_attention(1, 1, 17, 6, 4, 128, 100, 64, *([1] * 6), 0.0, 1, None, 0,
                                     None, None) == -1
     assert cdll.spec_kv_compact(1, 1, 8, 128, 10, 200, *([1] * 5), None, None) == -3
+
+
+def test_empty_batch_is_a_no_op(lib):
+    """B = 0 returns SPEC_OK before any launch, whatever the pointers."""
+    cdll = lib.load()
+    assert cdll.spec_build_tree(0, 0, 4, 4, 17, None, None, None, None, None, None, None, None,
+                                None, None, None) == 0
+    assert cdll.spec_tree_attention(1, 0, 17, 32, 32, 128, 1100, 1024, *([None] * 6), 0.0, None,
+                                    None, 0, None, None) == 0
+    assert cdll.spec_verify(0, 0, 17, 1000, 0, *([None] * 17), 0, None, None) == 0
+    assert cdll.spec_kv_compact(1, 0, 8, 128, 1100, 17, *([None] * 5), None, None) == 0

@@ -1,0 +1,115 @@
+"""GPU parity on the edge cases of the method, through the C ABI, against the oracle.
+
+- the largest tree (127 positions: two mask words) with ragged context lengths,
+  including a sequence with no context at all (its first key tile holds only
+  tree keys), in all three verify modes and a planted greedy path;
+- head dimension 64 on the bf16 path and a grouped fp32 case;
+- a star tree (every candidate a child of the root) in all modes;
+- a context that overflows the launch bound: that sequence gets zero rows and
+  the device status bit, the others stay exact;
+- B = 0 calls (host-only, in test_abi.py).
+Bar as in test_gpu_parity.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_attention_verification_beam_amd import pipeline, synth
+
+from test_gpu_parity import (assert_tree_equal, assert_verify_equal, attn_bar, log, oracle_tree,
+                             oracle_verify)
+
+pytestmark = pytest.mark.gpu
+
+MODES = ("greedy", "reject_path", "reject_recursive")
+
+
+def run_all_modes(gpu, inp, what, planted=True):
+    tr = oracle_tree(inp)
+    for mode in MODES:
+        step = pipeline.Step(inp, mode)
+        res = step.run(compact=False)
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_tree_equal(res, tr)
+        assert_verify_equal(res, oracle_verify(inp, tr, mode), f"{what} {mode}")
+        if mode == "greedy":
+            ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"],
+                                        tr["n_nodes"], tr["anc"])
+            attn_bar(res["attn"], ref, what)
+            k0, v0 = inp["k"].copy(), inp["v"].copy()
+            step.compact()
+            torch.cuda.synchronize()
+            new_ctx = oracle.kv_compact(k0, v0, inp["ctx_len"], res["acc_len"], res["acc_path"])
+            view = torch.int16 if step.k.dtype == torch.bfloat16 else torch.int32
+            assert np.array_equal(step.k.view(view).cpu().numpy().view(k0.dtype), k0)
+            assert np.array_equal(step.v.view(view).cpu().numpy().view(v0.dtype), v0)
+            assert np.array_equal(step.ctx_len.cpu().numpy(), new_ctx)
+    if planted:
+        # plant a full path so greedy accepts every node of one branch and the
+        # bonus token comes from the leaf
+        tgt = inp["tgt"].copy()
+        for b in range(inp["B"]):
+            t = int(tr["n_nodes"][b]) - 1          # the last node: walk its path
+            path = []
+            while t > 0:
+                path.append(t)
+                t = int(tr["parent"][b, t])
+            for t in path:
+                par = int(tr["parent"][b, t])
+                tgt[b, par, tr["token"][b, t]] = tgt[b, par].max() + 20.0
+        inp2 = dict(inp, tgt=tgt)
+        step = pipeline.Step(inp2, "greedy", with_kv=False)
+        res = step.run()
+        ref = oracle_verify(inp2, tr, "greedy")
+        assert_verify_equal(res, ref, f"{what} greedy planted")
+        assert ref["acc_len"].min() >= 1
+
+
+def test_largest_tree_ragged_context(gpu):
+    inp = synth.make_custom_inputs(9001, B=3, H=8, Hkv=2, D=128, V=3000, dtype="bf16",
+                                   ctx_lens=[0, 77, 300], tree="beams", W=18, L=7)
+    assert inp["T_cap"] == 127
+    log(f"case largest tree T_cap={inp['T_cap']} ctx={inp['ctx_len'].tolist()}")
+    run_all_modes(gpu, inp, "T_cap=127")
+
+
+def test_head_dim_64_bf16(gpu):
+    inp = synth.make_custom_inputs(9002, B=2, H=4, Hkv=1, D=64, V=2000, dtype="bf16",
+                                   ctx_lens=[200, 129], tree="beams", W=4, L=4)
+    log("case D=64 bf16 G=4")
+    run_all_modes(gpu, inp, "D=64")
+
+
+def test_fp32_grouped(gpu):
+    inp = synth.make_custom_inputs(9003, B=2, H=8, Hkv=2, D=32, V=1500, dtype="f32",
+                                   ctx_lens=[50, 0], tree="beams", W=3, L=5)
+    log("case fp32 G=4 D=32")
+    run_all_modes(gpu, inp, "fp32 GQA")
+
+
+def test_star_tree(gpu):
+    inp = synth.make_custom_inputs(9004, B=2, H=4, Hkv=4, D=128, V=4000, dtype="bf16",
+                                   ctx_lens=[130, 64], tree="explicit", parents=[0] * 40)
+    log("case star tree, 40 children of the root")
+    run_all_modes(gpu, inp, "star")
+
+
+def test_context_overflow_flags_one_sequence(gpu):
+    inp = synth.make_custom_inputs(9005, B=3, H=8, Hkv=8, D=128, V=1000, dtype="bf16",
+                                   ctx_lens=[100, 120, 90], tree="beams", W=4, L=3)
+    log("case context past the launch bound in sequence 1")
+    tr = oracle_tree(inp)
+    step = pipeline.Step(inp, "greedy")
+    step.build_tree()
+    step.ctx_len[1] = step.max_ctx + 1        # beyond the host bound of the launch
+    step.attention()
+    torch.cuda.synchronize()
+    status = int(step.status.item())
+    assert status & 0x8, gpu.decode_status(status)
+    got = step.out.float().cpu().numpy()
+    assert np.all(got[1] == 0)
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    for b in (0, 2):
+        attn_bar(got[b], ref[b], f"overflow case, sequence {b}")

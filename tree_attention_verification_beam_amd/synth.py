@@ -225,3 +225,49 @@ def make_inputs(wid: int, seed_offset: int = 0, *, with_kv: bool = True,
         out["k"] = conv(_normal(rngs["k"], (B, w.Hkv, cap, w.D)))
         out["v"] = conv(_normal(rngs["v"], (B, w.Hkv, cap, w.D)))
     return out
+
+
+def make_custom_inputs(seed: int, *, B: int, H: int, Hkv: int, D: int, V: int, dtype: str,
+                       ctx_lens, tree: str = "beams", W: int = 0, L: int = 0, parents=None,
+                       draft_sigma: float = 1.0) -> dict:
+    """Inputs of one step with free shapes, for edge cases of the parity tests.
+
+    tree = "beams": W beams of L tokens with shared prefixes drawn as in the
+    workloads.  tree = "explicit": every sequence uses the parent list
+    `parents` (node j+1's parent) with uniform tokens.  Each node's children
+    are drawn from that node's own draft row (dft_row = identity).  Context
+    lengths may differ per sequence; the cache holds the longest context plus
+    the tree.
+    """
+    ss = np.random.SeedSequence(seed)
+    rngs = dict(zip(STREAMS, [np.random.default_rng(s) for s in ss.spawn(len(STREAMS))]))
+    ctx_lens = np.asarray(ctx_lens, np.int32)
+    assert ctx_lens.shape == (B,)
+    if tree == "beams":
+        T_cap = 1 + W * L
+    else:
+        T_cap = 1 + len(parents)
+    cap = int(ctx_lens.max()) + T_cap
+    out = dict(wid=-1, name="custom", B=B, ctx=int(ctx_lens.max()), T_cap=T_cap, cap=cap, H=H,
+               Hkv=Hkv, D=D, V=V, dtype=dtype, tree=tree if tree == "beams" else "explicit",
+               modes=("greedy", "reject_path", "reject_recursive"))
+    out["root_token"] = rngs["tree"].integers(0, V, size=B, dtype=np.int64).astype(np.int32)
+    tgt = _normal(rngs["tgt"], (B, T_cap, V), 3.0)
+    out["tgt"] = tgt
+    if tree == "beams":
+        out["W"], out["L"] = W, L
+        out["beams"] = _draw_beams(rngs["tree"], B, W, L, V)
+    else:
+        out["cand_parent"] = np.tile(np.asarray(parents, np.int32), (B, 1))
+        out["cand_token"] = rngs["tree"].integers(0, V, size=(B, len(parents)),
+                                                  dtype=np.int64).astype(np.int32)
+    out["dft"] = tgt + _normal(rngs["dft"], (B, T_cap, V), draft_sigma)
+    out["dft_row"] = np.tile(np.arange(T_cap, dtype=np.int32), (B, 1))
+    out["u_node"] = exact_uniforms(rngs["u_node"], (B, T_cap))
+    out["u_final"] = exact_uniforms(rngs["u_final"], (B,))
+    out["ctx_len"] = ctx_lens.copy()
+    conv = (lambda a: a) if dtype == "f32" else f32_to_bf16_bits
+    out["q"] = conv(_normal(rngs["q"], (B, T_cap, H, D)))
+    out["k"] = conv(_normal(rngs["k"], (B, Hkv, cap, D)))
+    out["v"] = conv(_normal(rngs["v"], (B, Hkv, cap, D)))
+    return out
