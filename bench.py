@@ -15,8 +15,10 @@ stream, and the CPU oracle timed on the host as a baseline.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 from pathlib import Path
@@ -41,7 +43,33 @@ def parse():
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
+    ap.add_argument("--probe-mib", type=int, default=512,
+                    help="size of the plain copy that calibrates bandwidth and counters")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    src = ROOT / "tree_attention_verification_beam_amd" / "csrc" / "tree_attention.hip"
+    return hashlib.sha256(src.read_bytes()).hexdigest()
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per attention call from the committed rocprofv3 counter summary.
+
+    The summary (profiles/pmc_traffic_<workload>.md) holds FETCH_SIZE and
+    WRITE_SIZE per dispatch, scaled by what the same counters read for a plain
+    copy of known size, and the hash of the attention source they were taken on;
+    a different hash means the kernel changed since, and the figure is dropped.
+    """
+    path = ROOT / "profiles" / f"pmc_traffic_{workload}.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    h = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    v = re.search(r"traffic_bytes_per_call:\s*([0-9.eE+]+)", text)
+    if not h or not v or h.group(1) != kernel_source_hash():
+        return None
+    return float(v.group(1))
 
 
 def attention_bytes(inp, n_nodes):
@@ -127,6 +155,21 @@ def main():
         one_step(i)
     torch.cuda.synchronize()
 
+    # ---------------------------------------------------------------- copy calibration
+    # one plain streaming copy of known size: its rate is the platform's
+    # achievable HBM figure, and its counter readings calibrate FETCH/WRITE_SIZE
+    n_probe = args.probe_mib << 20
+    p_src = torch.empty(n_probe, dtype=torch.uint8, device=dev)
+    p_dst = torch.empty(n_probe, dtype=torch.uint8, device=dev)
+    sv.spec_copy_probe(p_src, p_dst, n_probe)
+    pa, pb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    pa.record(stream)
+    sv.spec_copy_probe(p_src, p_dst, n_probe)
+    pb.record(stream)
+    torch.cuda.synchronize()
+    probe_gbps = 2 * n_probe / (pa.elapsed_time(pb) * 1e-3) / 1e9
+    del p_src, p_dst
+
     # ---------------------------------------------------------------- timed steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -194,8 +237,10 @@ def main():
                    "draft_nodes_per_step": float(np.mean(n_draft)), "input_sets": n_sets},
         "roofline": {"bound": "hbm", "kernel": "spec_tree_attention", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "algorithmic_bytes_per_launch": a_avg,
+                     "traffic": counted_traffic(wl.name), "algorithmic_bytes_per_launch": a_avg,
                      "avg_launch_us": attn_avg_s * 1e6},
+        "copy_probe": {"bytes": 2 * n_probe, "GBps": probe_gbps,
+                       "frac_of_peak": probe_gbps / HBM_PEAK_GBPS},
         "breakdown_us": brk,
         "attention_verify": {
             "attention_GBps": a_avg / (brk["attention"] * 1e-6) / 1e9,

@@ -184,7 +184,8 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * fell within 1e-9 of a running-sum boundary).
  * A bad token or missing draft row raises a SPEC_DEV_* bit and the sequence
  * accepts nothing (acc_len 0, next_token = argmax p_0).
- * ws: spec_verify_workspace_size() bytes.
+ * ws: spec_verify_workspace_size() bytes (no initial contents needed).  Calls
+ * that overlap in time must not share a workspace.
  */
 size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R);
 int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, const float *dft,

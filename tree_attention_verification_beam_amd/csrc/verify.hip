@@ -8,22 +8,22 @@
 // becomes the residual max(0, p - q) / sum max(0, p - q).
 //
 // Kernels, in stream order:
-//   k_vprep   one workgroup per sequence: validates the tree against V and R,
-//             marks which draft rows are needed, resets the sequence's
-//             cross-workgroup counter.
 //   k_vstats  the vocabulary stream: every needed logits row is read once, in
 //             chunks; each chunk yields (max, argmax with the lowest index on
 //             ties, sum exp(l - max)).  Coalesced 16-byte loads; exp in fp32,
-//             sums in fp64.
-//   k_vselect P workgroups per sequence (P = 1 for greedy): merge the chunk
-//             partials into row statistics, gather p and q of every node's own
-//             token (fp64 exp), run the mode's tests and the path select, and
-//             do the residual passes and the inverse-CDF draw over the stop
+//             sums in fp64.  A draft row is read only when it is the draft row
+//             of a node with a child.
+//   k_vselect P workgroups per sequence (P = 1 for greedy): validate the tree,
+//             merge the chunk partials of the needed rows into row statistics
+//             (all threads, staged in LDS), gather p and q of every node's
+//             own token (fp64 exp), run the mode's tests and the path select,
+//             and do the residual passes and the inverse-CDF draw over the stop
 //             row pair in fp64.  With P > 1 the workgroups of a sequence split
 //             the vocabulary, publish per-pass partial sums and meet at a
-//             counter barrier; every workgroup then holds the same totals and
-//             takes the same decisions.  Such launches are cooperative, so all
-//             workgroups are resident; every wait is bounded.
+//             counter barrier (re-armed by k_vstats); every workgroup then
+//             holds the same totals and takes the same decisions.  Such
+//             launches are cooperative, so all workgroups are resident; every
+//             wait is bounded.
 #include "common.hpp"
 
 namespace spec {
@@ -33,6 +33,7 @@ constexpr int kStatThreads = 256;
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxP = 32;
+constexpr int kMergeEntries = 1024;  // chunk partials staged in LDS per merge batch
 constexpr size_t kSyncStride = 2048;  // bytes of sync area per sequence
 constexpr double kNearTie = 1e-5;
 constexpr double kCdfNearTie = 1e-9;
@@ -44,28 +45,12 @@ struct Partial {
   int arg;   // lowest index attaining m
 };
 
-// Partials cross workgroups through the device-coherent level (two 64-bit words).
-__device__ inline void store_partial(Partial* p, double S, float m, int arg) {
-  uint64_t* w = reinterpret_cast<uint64_t*>(p);
-  store_coherent(w, __double_as_longlong(S));
-  store_coherent(w + 1, (uint64_t)__float_as_uint(m) | ((uint64_t)(uint32_t)arg << 32));
-}
-__device__ inline Partial load_partial(const Partial* p) {
-  const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
-  const uint64_t a = load_coherent(w), b = load_coherent(w + 1);
-  Partial r;
-  r.S = __longlong_as_double((long long)a);
-  r.m = __uint_as_float((uint32_t)b);
-  r.arg = (int)(uint32_t)(b >> 32);
-  return r;
-}
-
 struct VerifyPlan {
   int ept;       // floats per thread in k_vstats
   int chunk;     // floats per chunk
   int n_chunks;  // chunks per row
   long n_units;  // rows: B*T_cap target rows, then B*R draft rows
-  size_t off_part, off_row, off_cnt, off_need, off_bad, off_sync, total;
+  size_t off_part, off_sync, total;
 };
 
 VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
@@ -73,21 +58,19 @@ VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
   p.n_units = (long)B * T_cap + (long)B * Rr;
   p.ept = 32;
-  while (p.ept > 4 && p.n_units * ((V + p.ept * kStatThreads - 1) / (p.ept * kStatThreads)) < 2048)
+  // about one workgroup per CU at least; larger chunks keep the row merges short
+  while (p.ept > 4 && p.n_units * ((V + p.ept * kStatThreads - 1) / (p.ept * kStatThreads)) < 256)
     p.ept >>= 1;
   p.chunk = p.ept * kStatThreads;
   p.n_chunks = (V + p.chunk - 1) / p.chunk;
+  while (p.n_chunks > kMergeEntries && p.ept < 32) {  // very large vocabularies
+    p.ept <<= 1;
+    p.chunk = p.ept * kStatThreads;
+    p.n_chunks = (V + p.chunk - 1) / p.chunk;
+  }
   size_t off = 0;
   p.off_part = off;
   off += round_up((size_t)p.n_units * p.n_chunks * sizeof(Partial), 256);
-  p.off_row = off;
-  off += round_up((size_t)p.n_units * sizeof(Partial), 256);
-  p.off_cnt = off;
-  off += round_up((size_t)p.n_units * sizeof(int32_t), 256);
-  p.off_need = off;
-  off += round_up((size_t)B * (Rr > 0 ? Rr : 1) * sizeof(int32_t), 256);
-  p.off_bad = off;
-  off += round_up((size_t)B * sizeof(int32_t), 256);
   p.off_sync = off;
   off += (size_t)B * kSyncStride;
   p.total = off;
@@ -145,71 +128,15 @@ __device__ double block_exclusive_scan_f64(double v, double* s_buf, double& excl
   return total;
 }
 
-// ------------------------------------------------------------------ k_vprep
-
-__global__ __launch_bounds__(SPEC_MAX_TREE) void k_vprep(
-    int mode, int T_cap, int V, int R, const int32_t* __restrict__ n_nodes,
-    const int32_t* __restrict__ parent, const int32_t* __restrict__ token,
-    const int32_t* __restrict__ depth, const int32_t* __restrict__ dft_row,
-    int32_t* __restrict__ need, int32_t* __restrict__ seq_bad, unsigned char* __restrict__ sync,
-    int32_t* __restrict__ cnt, int B, int32_t* __restrict__ status) {
-  __shared__ int s_has_child[SPEC_MAX_TREE];
-  __shared__ int s_bad;
-  const int b = blockIdx.x, t = threadIdx.x;
-  const int T = n_nodes[b];
-  const int Rr = mode == SPEC_GREEDY ? 0 : R;
-  if (t == 0) s_bad = 0;
-  s_has_child[t] = 0;
-  for (int r = t; r < Rr; r += SPEC_MAX_TREE) {
-    need[(size_t)b * Rr + r] = 0;
-    cnt[(size_t)B * T_cap + (size_t)b * Rr + r] = 0;
-  }
-  for (int r = t; r < T_cap; r += SPEC_MAX_TREE) cnt[(size_t)b * T_cap + r] = 0;
-  __syncthreads();
-  if (T < 1 || T > T_cap) {
-    if (t == 0) {
-      s_bad = SPEC_DEV_BAD_TREE;
-    }
-  } else if (t < T) {
-    const size_t i = (size_t)b * T_cap + t;
-    if (t > 0) {
-      const int p = parent[i];
-      if (p < 0 || p >= t) {
-        atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
-      } else {
-        const int dp = p == 0 ? 0 : depth[(size_t)b * T_cap + p];
-        if (depth[i] != dp + 1) atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
-        s_has_child[p] = 1;
-      }
-      const int x = token[i];
-      if (x < 0 || x >= V) atomicOr(&s_bad, SPEC_DEV_BAD_TOKEN);
-    }
-  }
-  __syncthreads();
-  if (Rr > 0 && !s_bad && t < T && s_has_child[t]) {
-    const int r = dft_row[(size_t)b * T_cap + t];
-    if (r < 0 || r >= Rr) atomicOr(&s_bad, SPEC_DEV_BAD_ROW);
-    else need[(size_t)b * Rr + r] = 1;
-  }
-  __syncthreads();
-  if (t == 0) {
-    seq_bad[b] = s_bad;
-    if (s_bad) raise_status(status, s_bad);
-    // reset the cross-workgroup counter of this sequence
-    __hip_atomic_store(reinterpret_cast<int*>(sync + (size_t)b * kSyncStride), 0, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
 // ------------------------------------------------------------------ k_vstats
 
 template <int EPT, bool VEC>
 __global__ __launch_bounds__(kStatThreads) void k_vstats(
     int B, int T_cap, int V, int Rr, int n_chunks, const float* __restrict__ tgt,
     const float* __restrict__ dft, const int32_t* __restrict__ n_nodes,
-    const int32_t* __restrict__ need, Partial* __restrict__ part, Partial* __restrict__ rows,
-    int32_t* __restrict__ cnt) {
-  __shared__ int s_last;
+    const int32_t* __restrict__ parent, const int32_t* __restrict__ dft_row,
+    Partial* __restrict__ part, unsigned char* __restrict__ sync) {
+  __shared__ int s_need;
   __shared__ float s_m[kStatThreads / 64];
   __shared__ int s_a[kStatThreads / 64];
   __shared__ double s_s[kStatThreads / 64];
@@ -217,16 +144,30 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
   const int c = blockIdx.x - (int)(unit * n_chunks);
   const float* row;
   const long n_tgt = (long)B * T_cap;
+  const int tid = threadIdx.x;
   if (unit < n_tgt) {
     const int b = (int)(unit / T_cap), t = (int)(unit - (long)b * T_cap);
     if (t > 0 && t >= n_nodes[b]) return;
+    // the sequence's root row, first chunk: re-arm the select's meeting counter
+    if (t == 0 && c == 0 && tid == 0)
+      __hip_atomic_store(reinterpret_cast<int*>(sync + (size_t)b * kSyncStride), 0,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     row = tgt + unit * (long)V;
   } else {
+    // a draft row is needed iff it is the draft row of some node with a child
     const long u2 = unit - n_tgt;
-    if (!need[u2]) return;
+    const int b = (int)(u2 / Rr), r = (int)(u2 - (long)b * Rr);
+    if (tid == 0) s_need = 0;
+    __syncthreads();
+    const int T = min(n_nodes[b], T_cap);
+    for (int u = 1 + tid; u < T; u += kStatThreads) {
+      const int p = parent[(size_t)b * T_cap + u];
+      if (p >= 0 && p < u && dft_row[(size_t)b * T_cap + p] == r) s_need = 1;
+    }
+    __syncthreads();
+    if (!s_need) return;
     row = dft + u2 * (long)V;
   }
-  const int tid = threadIdx.x;
   const int base = c * EPT * kStatThreads;
   float x[EPT];
   int idx0[EPT / 4];
@@ -287,40 +228,11 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
   if (tid == 0) {
     double tot = 0.0;
     for (int w = 0; w < kStatThreads / 64; ++w) tot += s_s[w];
-    // publish the chunk's partial at the coherent level, then count it; the
-    // workgroup that completes a row's last chunk merges the row
-    store_partial(part + unit * n_chunks + c, tot, m, a);
-    wait_stores_done();
-    s_last = atomicAdd(cnt + unit, 1) == n_chunks - 1;
-  }
-  __syncthreads();
-  if (!s_last || wave != 0) return;
-  // one wave: lanes over the chunks (increasing index within a lane), then the
-  // wave combines (max, lowest argmax, sum rescaled to the row maximum) in fp64
-  float mr = -INFINITY;
-  int ar = 0x7fffffff;
-  double Sr = 0.0;
-  for (int cc = lane; cc < n_chunks; cc += 64) {
-    const Partial q = load_partial(part + unit * n_chunks + cc);
-    if (q.m > mr) {
-      Sr = (mr == -INFINITY ? 0.0 : Sr * exp((double)mr - (double)q.m)) + q.S;
-      mr = q.m;
-      ar = q.arg;
-    } else if (q.m != -INFINITY) {
-      Sr += q.S * exp((double)q.m - (double)mr);
-    }
-  }
-  float mw = mr;
-  int aw = ar;
-  wave_argmax(mw, aw);
-  const double Sw = wave_sum_f64(mr == -INFINITY ? 0.0 : Sr * exp((double)mr - (double)mw));
-  if (lane == 0) {
-    Partial r;
-    r.S = Sw;
-    r.m = mw;
-    r.arg = aw;
-    rows[unit] = r;
-    cnt[unit] = 0;
+    Partial p;
+    p.S = tot;
+    p.m = m;
+    p.arg = a;
+    part[unit * n_chunks + c] = p;
   }
 }
 
@@ -337,8 +249,7 @@ struct SelArgs {
   const int32_t* depth;
   const float* u_node;
   const float* u_final;
-  const Partial* rows;
-  const int32_t* seq_bad;
+  const Partial* part;
   unsigned char* sync;
   int32_t* acc_len;
   int32_t* acc_path;
@@ -364,11 +275,16 @@ struct SelShared {
   double pt[SPEC_MAX_TREE];
   double qt[SPEC_MAX_TREE];
   int dec[SPEC_MAX_TREE];
-  int chain[SPEC_MAX_TREE];
   double red[2 * kSelWaves];
   double scan[kSelThreads];
   double slots[2 * kMaxP];
   double invN[64];
+  // row-statistics merge: jobs are the needed rows, entries their chunk partials
+  Partial ent[kMergeEntries];
+  int job_unit[2 * SPEC_MAX_TREE];
+  int job_node[2 * SPEC_MAX_TREE];  // node t; draft rows of node t stored as -1 - t
+  float job_m[2 * SPEC_MAX_TREE];
+  int n_jobs;
   int near_count;
   int stop;
 };
@@ -614,9 +530,10 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   sy.status = A.status;
   const bool lead = w == 0;
 
-  const bool bad = A.seq_bad[b] != 0;
-  const int T = bad ? 1 : A.n_nodes[b];
   const size_t nb = (size_t)b * T_cap;
+  __shared__ int s_bad;
+  const int T_in = A.n_nodes[b];
+  int T = T_in < 1 ? 1 : (T_in > T_cap ? T_cap : T_in);
 
   // ---------------------------------------------------------------- tree + row stats
   for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) {
@@ -625,7 +542,10 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     sh.pt[t] = 0.0;
     sh.qt[t] = 0.0;
   }
-  if (tid == 0) sh.near_count = 0;
+  if (tid == 0) {
+    sh.near_count = 0;
+    s_bad = (T_in < 1 || T_in > T_cap) ? SPEC_DEV_BAD_TREE : 0;
+  }
   __syncthreads();
   for (int t = tid; t < T; t += kSelThreads) {
     sh.par[t] = t == 0 ? -1 : A.parent[nb + t];
@@ -633,21 +553,99 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     sh.dep[t] = t == 0 ? 0 : A.depth[nb + t];
   }
   __syncthreads();
-  for (int t = tid + 1; t < T; t += kSelThreads) atomicAdd(&sh.nch[sh.par[t]], 1);
-  __syncthreads();
-  // row statistics, merged per row by the vocabulary pass
-  for (int t = tid; t < T; t += kSelThreads) {
-    const Partial r = A.rows[nb + t];
-    sh.m_p[t] = r.m;
-    sh.arg_p[t] = r.arg;
-    sh.S_p[t] = r.S;
-    if (MODE != SPEC_GREEDY && sh.nch[t] > 0) {
-      const Partial rq = A.rows[(size_t)A.B * T_cap + (size_t)b * A.Rr + A.dft_row[nb + t]];
-      sh.m_q[t] = rq.m;
-      sh.S_q[t] = rq.S;
+  // validate the tree against the vocabulary and the draft rows; a bad
+  // sequence accepts nothing and takes the greedy token at the root
+  for (int t = tid + 1; t < T; t += kSelThreads) {
+    const int p = sh.par[t];
+    if (p < 0 || p >= t) {
+      atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+    } else {
+      if (sh.dep[t] != sh.dep[p] + 1) atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+      atomicAdd(&sh.nch[p], 1);
     }
+    if (sh.tok[t] < 0 || sh.tok[t] >= V) atomicOr(&s_bad, SPEC_DEV_BAD_TOKEN);
   }
   __syncthreads();
+  if (MODE != SPEC_GREEDY) {
+    for (int t = tid; t < T; t += kSelThreads) {
+      if (sh.nch[t] == 0) continue;
+      const int r = A.dft_row[nb + t];
+      if (r < 0 || r >= A.Rr) atomicOr(&s_bad, SPEC_DEV_BAD_ROW);
+    }
+    __syncthreads();
+  }
+  const bool bad = s_bad != 0;
+  if (bad) {
+    if (lead && tid == 0) raise_status(A.status, s_bad);
+    T = 1;
+    for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) sh.nch[t] = 0;
+    __syncthreads();
+  }
+  // Row statistics from the vocabulary pass's chunk partials, with all threads:
+  // the partials of a batch of rows are staged in LDS, then per row the
+  // maximum and lowest argmax (chunks in index order), per partial its sum
+  // rescaled to the row maximum (fp64), and per row the total.
+  if (tid == 0) sh.n_jobs = T;
+  for (int t = tid; t < T; t += kSelThreads) {
+    sh.job_unit[t] = (int)(nb + t);
+    sh.job_node[t] = t;
+  }
+  __syncthreads();
+  if (MODE != SPEC_GREEDY) {
+    for (int t = tid; t < T; t += kSelThreads) {
+      if (sh.nch[t] == 0) continue;
+      const int j = atomicAdd(&sh.n_jobs, 1);
+      sh.job_unit[j] = (int)((size_t)A.B * T_cap + (size_t)b * A.Rr + A.dft_row[nb + t]);
+      sh.job_node[j] = -1 - t;
+    }
+    __syncthreads();
+  }
+  {
+    const int n_jobs = sh.n_jobs, nc = A.n_chunks;
+    const int per_batch = min(kMergeEntries / nc, 2 * SPEC_MAX_TREE);
+    for (int j0 = 0; j0 < n_jobs; j0 += per_batch) {
+      const int nj = min(per_batch, n_jobs - j0);
+      for (int e = tid; e < nj * nc; e += kSelThreads) {
+        const int j = j0 + e / nc, cc = e - (e / nc) * nc;
+        sh.ent[e] = A.part[(size_t)sh.job_unit[j] * nc + cc];
+      }
+      __syncthreads();
+      for (int k = tid; k < nj; k += kSelThreads) {
+        float m = -INFINITY;
+        int arg = 0;
+        for (int cc = 0; cc < nc; ++cc) {
+          const Partial& q = sh.ent[k * nc + cc];
+          if (q.m > m) {
+            m = q.m;
+            arg = q.arg;
+          }
+        }
+        sh.job_m[k] = m;
+        const int node = sh.job_node[j0 + k];
+        if (node >= 0) {
+          sh.m_p[node] = m;
+          sh.arg_p[node] = arg;
+        } else {
+          sh.m_q[-1 - node] = m;
+        }
+      }
+      __syncthreads();
+      for (int e = tid; e < nj * nc; e += kSelThreads) {
+        const int k = e / nc;
+        const float mc = sh.ent[e].m;
+        sh.ent[e].S = mc == -INFINITY ? 0.0 : sh.ent[e].S * exp((double)mc - (double)sh.job_m[k]);
+      }
+      __syncthreads();
+      for (int k = tid; k < nj; k += kSelThreads) {
+        double S = 0.0;
+        for (int cc = 0; cc < nc; ++cc) S += sh.ent[k * nc + cc].S;
+        const int node = sh.job_node[j0 + k];
+        if (node >= 0) sh.S_p[node] = S;
+        else sh.S_q[-1 - node] = S;
+      }
+      __syncthreads();
+    }
+  }
   // p and q of every node's own token under its parent (fp64 exp, merged sums)
   for (int t = tid + 1; t < T; t += kSelThreads) {
     const int s = sh.par[t], x = sh.tok[t];
@@ -682,15 +680,18 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
       sh.dec[t] = acc;
     }
     __syncthreads();
-    if (tid == 0) {
-      sh.chain[0] = 1;
-      int best = 0;
-      for (int t = 1; t < T; ++t) {
-        sh.chain[t] = sh.dec[t] && sh.chain[sh.par[t]];
-        if (sh.chain[t] && sh.dep[t] > sh.dep[best]) best = t;
-      }
-      sh.stop = best;
+    // a node survives when it and all its ancestors are accepted; the deepest
+    // survivor wins, the lowest node index on ties (one thread per node, each
+    // walking its own ancestors, then a max over keys depth*1024 + (1023 - t))
+    if (tid == 0) sh.stop = 1023;  // key of the root: depth 0, node 0
+    __syncthreads();
+    for (int t = tid + 1; t < T; t += kSelThreads) {
+      int ok = 1;
+      for (int u = t; u > 0 && ok; u = sh.par[u]) ok = sh.dec[u];
+      if (ok) atomicMax(&sh.stop, sh.dep[t] * 1024 + (1023 - t));
     }
+    __syncthreads();
+    if (tid == 0) sh.stop = 1023 - (sh.stop & 1023);
     __syncthreads();
     stop = sh.stop;
     if (MODE == SPEC_REJECT_PATH && !bad) {
@@ -851,15 +852,16 @@ int choose_p(int mode, int B, int V) {
 
 template <int EPT>
 void launch_stats(const VerifyPlan& pl, bool vec, int B, int T_cap, int V, int Rr,
-                  const float* tgt, const float* dft, const int32_t* n_nodes, const int32_t* need,
-                  Partial* part, Partial* rows, int32_t* cnt, hipStream_t s) {
+                  const float* tgt, const float* dft, const int32_t* n_nodes,
+                  const int32_t* parent, const int32_t* dft_row, Partial* part,
+                  unsigned char* sync, hipStream_t s) {
   const dim3 grid((unsigned)(pl.n_units * pl.n_chunks));
   if (vec)
     hipLaunchKernelGGL((k_vstats<EPT, true>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
-                       pl.n_chunks, tgt, dft, n_nodes, need, part, rows, cnt);
+                       pl.n_chunks, tgt, dft, n_nodes, parent, dft_row, part, sync);
   else
     hipLaunchKernelGGL((k_vstats<EPT, false>), grid, dim3(kStatThreads), 0, s, B, T_cap, V, Rr,
-                       pl.n_chunks, tgt, dft, n_nodes, need, part, rows, cnt);
+                       pl.n_chunks, tgt, dft, n_nodes, parent, dft_row, part, sync);
 }
 
 }  // namespace
@@ -894,22 +896,19 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
   char* w = static_cast<char*>(ws);
   Partial* part = reinterpret_cast<Partial*>(w + pl.off_part);
-  int32_t* need = reinterpret_cast<int32_t*>(w + pl.off_need);
-  Partial* rows = reinterpret_cast<Partial*>(w + pl.off_row);
-  int32_t* cnt = reinterpret_cast<int32_t*>(w + pl.off_cnt);
-  int32_t* seq_bad = reinterpret_cast<int32_t*>(w + pl.off_bad);
   unsigned char* sync = reinterpret_cast<unsigned char*>(w + pl.off_sync);
   hipStream_t s = as_stream(stream);
 
-  hipLaunchKernelGGL(k_vprep, dim3(B), dim3(SPEC_MAX_TREE), 0, s, mode, T_cap, V, Rr, n_nodes,
-                     parent, token, depth, dft_row, need, seq_bad, sync, cnt, B, status);
   const bool vec = (V % 4 == 0) && aligned(tgt, 16) && (Rr == 0 || aligned(dft, 16));
+#define SPEC_STATS(E)                                                                       \
+  launch_stats<E>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, parent, dft_row, part, sync, s)
   switch (pl.ept) {
-    case 32: launch_stats<32>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
-    case 16: launch_stats<16>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
-    case 8: launch_stats<8>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
-    default: launch_stats<4>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, need, part, rows, cnt, s); break;
+    case 32: SPEC_STATS(32); break;
+    case 16: SPEC_STATS(16); break;
+    case 8: SPEC_STATS(8); break;
+    default: SPEC_STATS(4); break;
   }
+#undef SPEC_STATS
   int rc = launch_status();
   if (rc != SPEC_OK) return rc;
 
@@ -929,8 +928,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   A.depth = depth;
   A.u_node = u_node;
   A.u_final = u_final;
-  A.rows = rows;
-  A.seq_bad = seq_bad;
+  A.part = part;
   A.sync = sync;
   A.acc_len = acc_len;
   A.acc_path = acc_path;
