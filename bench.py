@@ -2,7 +2,9 @@
 
 A step is the whole hot path over one batch of synthetic input: spec_build_tree,
 spec_tree_attention, spec_verify and spec_kv_compact, enqueued on one stream,
-preceded by restoring the sequence's context length (the commit advances it).
+preceded by restoring the sequence's context length (the commit advances it)
+with the library's copy kernel.  The calls are marshalled once (prepared), so
+the host issues a step faster than the GPU runs it.
 Inputs already sit in HBM.  To keep the measurement honest about HBM (the
 256 MB Infinity Cache would otherwise hold a small workload), the timed steps
 rotate over several independent input sets whose total exceeds twice the
@@ -139,11 +141,16 @@ def main():
         print(f"[bench] set {s + 1}/{n_sets} ready", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream(dev)
+    for _, st in steps_all:
+        st.prepare(stream)
 
     def one_step(i):
         inp, st = steps_all[i % n_sets]
-        st.ctx_len.copy_(st.ctx0, non_blocking=True)
-        st.launch(compact=True)
+        st.p_reset()       # the commit advanced ctx_len: restore it
+        st.p_build()
+        st.p_attention()
+        st.p_verify()
+        st.p_compact()
 
     # tree sizes (outside any timed region)
     for i in range(n_sets):
@@ -177,13 +184,13 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         inp, st = steps_all[i % n_sets]
-        st.ctx_len.copy_(st.ctx0, non_blocking=True)
-        st.build_tree()
+        st.p_reset()
+        st.p_build()
         ev[i][0].record(stream)
-        st.attention()
+        st.p_attention()
         ev[i][1].record(stream)
-        st.verify()
-        st.compact()
+        st.p_verify()
+        st.p_compact()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -197,8 +204,8 @@ def main():
     evs = {n: [] for n in names}
     for i in range(min(args.steps, 4 * n_sets)):
         inp, st = steps_all[i % n_sets]
-        st.ctx_len.copy_(st.ctx0, non_blocking=True)
-        for n, fn in zip(names, (st.build_tree, st.attention, st.verify, st.compact)):
+        st.p_reset()
+        for n, fn in zip(names, (st.p_build, st.p_attention, st.p_verify, st.p_compact)):
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             fn()

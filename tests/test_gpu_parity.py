@@ -126,7 +126,7 @@ def test_reduced_workload(gpu, wid, seed):
             vv = step.v.view(torch.int16 if step.v.dtype == torch.bfloat16 else torch.int32)
             assert np.array_equal(kk.cpu().numpy().view(k0.dtype), k0)
             assert np.array_equal(vv.cpu().numpy().view(v0.dtype), v0)
-            assert np.array_equal(step.ctx_len.cpu().numpy(), new_ctx)
+            assert np.array_equal(step.ctx_len[:inp["B"]].cpu().numpy(), new_ctx)
             assert int(step.status.item()) == 0
     if inp["tree"] == "beams":
         tgt = plant_greedy(inp, tr, seed)
@@ -188,7 +188,7 @@ def test_full_size(gpu, full):
         if n:
             assert torch.equal(step.k[b][:, ctx[b] + 1:ctx[b] + n + 1], k_before[b][:, src])
         assert torch.equal(step.k[b][:, :ctx[b] + 1], k_before[b][:, :ctx[b] + 1])
-    assert np.array_equal(step.ctx_len.cpu().numpy(), ctx + res["acc_len"] + 1)
+    assert np.array_equal(step.ctx_len[:inp["B"]].cpu().numpy(), ctx + res["acc_len"] + 1)
     assert int(step.status.item()) == 0
 
 

@@ -144,3 +144,38 @@ def spec_copy_probe(src, dst, n_bytes, stream=None):
 
 def decode_status(word: int) -> list[str]:
     return [name for bit, name in DEV_BITS.items() if word & bit]
+
+
+class Prepared:
+    """A C-ABI call with its arguments marshalled once (device addresses, sizes
+    and the stream fixed at preparation time), for loops that issue the same
+    call many times: calling it costs one ctypes call and a status check."""
+
+    def __init__(self, name: str, *args):
+        lib = load()
+        fn = getattr(lib, name)
+        self.name = name
+        self.fn = fn
+        conv = []
+        for a, t in zip(args, SIGNATURES[name][1]):
+            if t is _vp:
+                conv.append(_vp(_ptr(a)))
+            elif t is _c_float:
+                conv.append(_c_float(a))
+            elif t is _c_size:
+                conv.append(_c_size(a))
+            else:
+                conv.append(_c_int(a))
+        assert len(conv) == len(SIGNATURES[name][1]), name
+        self.args = tuple(conv)
+
+    def __call__(self):
+        rc = self.fn(*self.args)
+        if rc != 0:
+            raise SpecError(self.name, rc)
+
+
+def prepare(name: str, *args, stream=None) -> Prepared:
+    """Prepared(name, *args) with the stream (torch's current one by default)
+    appended as the last argument, as every launching entry point takes it."""
+    return Prepared(name, *args, _stream(stream))
