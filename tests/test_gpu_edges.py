@@ -113,3 +113,18 @@ def test_context_overflow_flags_one_sequence(gpu):
                                 tr["anc"])
     for b in (0, 2):
         attn_bar(got[b], ref[b], f"overflow case, sequence {b}")
+
+
+def test_large_batch_large_vocab(gpu):
+    """Many sequences with a large vocabulary: each sequence gets few select
+    workgroups, so their vocabulary slices exceed what the register cache of
+    the row pair holds and the residual passes read the rows from memory."""
+    inp = synth.make_custom_inputs(9006, B=64, H=1, Hkv=1, D=64, V=100000, dtype="bf16",
+                                   ctx_lens=[16] * 64, tree="beams", W=2, L=2)
+    log("case B=64, V=100000 (uncached residual passes)")
+    tr = oracle_tree(inp)
+    for mode in ("reject_path", "reject_recursive"):
+        step = pipeline.Step(inp, mode, with_kv=False)
+        res = step.run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_verify_equal(res, oracle_verify(inp, tr, mode), f"B=64 V=1e5 {mode}")

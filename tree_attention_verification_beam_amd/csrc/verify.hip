@@ -239,7 +239,7 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
 // ------------------------------------------------------------------ k_vselect
 
 struct SelArgs {
-  int B, T_cap, V, Rr, n_chunks, P;
+  int B, T_cap, V, Rr, n_chunks, P, cache;
   const float* tgt;
   const float* dft;
   const int32_t* dft_row;
@@ -514,6 +514,186 @@ __device__ bool pass_draw(const RowPair& rp, int k, const double* invN, double u
   return true;
 }
 
+// ------------------------------------------------------------------ cached row pair
+// When a workgroup's slice of the vocabulary fits, every thread keeps its
+// contiguous range of the stop row pair in registers, in fp64: the target side
+// (p, then each residual) and the draft side q.  The exponentials are taken
+// once per node; each residual pass is then a few FMAs per entry, applied in
+// the same operation order as eval_r.
+constexpr int kCacheE = 20;  // entries per thread
+
+struct RowCache {
+  double r[kCacheE];
+  double q[kCacheE];
+  int v0, n;
+};
+
+// this thread's contiguous range of its workgroup's slice (the draw's partition)
+__device__ inline void cache_range(RowCache& c, int V, const SeqSync& sy) {
+  const Slice sl = slice_of(V, sy.P, sy.w);
+  const int per = (sl.hi - sl.lo + kSelThreads - 1) / kSelThreads;
+  c.v0 = sl.lo + (int)threadIdx.x * per;
+  c.n = max(0, min(sl.hi, c.v0 + per) - c.v0);
+}
+
+// exp(l - m) of the row pair (q side only when with_q); with `normalise` the
+// fp64 totals are exchanged and both sides become p and q
+__device__ void cache_load(RowCache& c, RowPair& rp, bool with_q, bool normalise, SeqSync& sy,
+                           SelShared& sh) {
+  double a = 0.0, bq = 0.0;
+#pragma unroll
+  for (int e = 0; e < kCacheE; ++e) {
+    c.r[e] = 0.0;
+    c.q[e] = 0.0;
+    if (e < c.n) {
+      c.r[e] = exp((double)rp.lp[c.v0 + e] - rp.mp);
+      a += c.r[e];
+      if (with_q) {
+        c.q[e] = exp((double)rp.lq[c.v0 + e] - rp.mq);
+        bq += c.q[e];
+      }
+    }
+  }
+  if (!normalise) return;
+  block_sum2_f64(a, bq, sh.red);
+  sy.exchange(a, bq, sh.slots);
+  double ta = 0.0, tb = 0.0;
+  for (int i = 0; i < sy.P; ++i) {
+    ta += sh.slots[2 * i];
+    tb += sh.slots[2 * i + 1];
+  }
+  rp.invSp = 1.0 / ta;
+  rp.invSq = 1.0 / tb;
+#pragma unroll
+  for (int e = 0; e < kCacheE; ++e) {
+    c.r[e] *= rp.invSp;
+    c.q[e] *= rp.invSq;
+  }
+  __syncthreads();
+}
+
+// sum over the vocabulary of max(0, r - q), the next residual's normaliser
+__device__ double cache_residual_mass(const RowCache& c, SeqSync& sy, SelShared& sh) {
+  double a = 0.0;
+#pragma unroll
+  for (int e = 0; e < kCacheE; ++e) {
+    const double w = c.r[e] - c.q[e];
+    if (w > 0.0) a += w;
+  }
+  a = block_sum_f64(a, sh.red);
+  sy.exchange(a, 0.0, sh.slots);
+  double t = 0.0;
+  for (int i = 0; i < sy.P; ++i) t += sh.slots[2 * i];
+  __syncthreads();
+  return t;
+}
+
+// one rejection: r <- max(0, r - q) / N
+__device__ inline void cache_residual_step(RowCache& c, double invN) {
+#pragma unroll
+  for (int e = 0; e < kCacheE; ++e) {
+    const double w = c.r[e] - c.q[e];
+    c.r[e] = w > 0.0 ? w * invN : 0.0;
+  }
+}
+
+__device__ inline double cache_weight(const RowCache& c, int e, bool resid) {
+  if (!resid) return c.r[e];
+  const double w = c.r[e] - c.q[e];
+  return w > 0.0 ? w : 0.0;
+}
+
+// The inverse-CDF draw of pass_draw over cached weights: r itself (resid ==
+// false) or max(0, r - q).
+__device__ bool cache_draw(const RowCache& c, bool resid, double u, SeqSync& sy, SelShared& sh,
+                           int V, int* out_tok, int* out_near, double* total_out) {
+  const Slice sl = slice_of(V, sy.P, sy.w);
+  double mine = 0.0;
+#pragma unroll
+  for (int e = 0; e < kCacheE; ++e)
+    if (e < c.n) mine += cache_weight(c, e, resid);
+  double excl;
+  const double slice_total = block_exclusive_scan_f64(mine, sh.scan, excl);
+  (void)excl;
+  sy.exchange(slice_total, 0.0, sh.slots);
+  double total = 0.0;
+  for (int i = 0; i < sy.P; ++i) total += sh.slots[2 * i];
+  *total_out = total;
+  if (!(total > 0.0)) {
+    __syncthreads();
+    return false;
+  }
+  const double thr = u * total;
+  const double eps = kCdfNearTie * total;
+  double base = 0.0;
+  int js = -1, jlast = -1;
+  double base_last = 0.0;
+  for (int i = 0; i < sy.P; ++i) {
+    const double ti = sh.slots[2 * i];
+    if (ti > 0.0) {
+      jlast = i;
+      base_last = base;
+    }
+    if (js < 0 && ti > 0.0 && base + ti > thr) js = i;
+    if (js < 0) base += ti;
+  }
+  const bool overshoot = js < 0;
+  if (overshoot) {
+    js = jlast;
+    base = base_last;
+  }
+  __syncthreads();
+  if (js != sy.w) return false;
+  __shared__ int s_found_tok, s_found_near, s_last;
+  if (threadIdx.x == 0) {
+    s_found_tok = -1;
+    s_found_near = 0;
+    s_last = -1;
+  }
+  __syncthreads();
+  const double lo_run = base + (threadIdx.x > 0 ? sh.scan[threadIdx.x - 1] : 0.0);
+  const double hi_run = base + sh.scan[threadIdx.x];
+  if (!overshoot && mine > 0.0 && lo_run <= thr && thr < hi_run) {
+    double run = lo_run;
+    int found = -1, last_pos = -1, near = 1;
+    bool done = false;
+#pragma unroll
+    for (int e = 0; e < kCacheE; ++e) {
+      if (done || e >= c.n) continue;
+      const double w = cache_weight(c, e, resid);
+      if (!(w > 0.0)) continue;
+      last_pos = c.v0 + e;
+      const double before = run;
+      run += w;
+      if (run > thr) {
+        found = c.v0 + e;
+        near = (fabs(run - thr) < eps || fabs(before - thr) < eps) ? 1 : 0;
+        done = true;
+      }
+    }
+    s_found_tok = found >= 0 ? found : last_pos;
+    s_found_near = near;
+  }
+  __syncthreads();
+  if (s_found_tok < 0) {
+    // overshoot through rounding: the last token with positive weight of this slice
+    int last = -1;
+#pragma unroll
+    for (int e = 0; e < kCacheE; ++e)
+      if (e < c.n && cache_weight(c, e, resid) > 0.0) last = c.v0 + e;
+    if (last >= 0) atomicMax(&s_last, last);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      s_found_tok = s_last < 0 ? sl.lo : s_last;
+      s_found_near = 1;
+    }
+    __syncthreads();
+  }
+  *out_tok = s_found_tok;
+  *out_near = s_found_near;
+  return true;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   __shared__ SelShared sh;
@@ -664,6 +844,9 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   int draw_k = -1;          // -1: draw from p_stop; k >= 0: from max(0, r_k - q)
   const double* invN = sh.invN;
   RowPair rp{};
+  RowCache rc;
+  bool cached = false;  // rc holds the current node's normalised pair (residual after k steps)
+  cache_range(rc, V, sy);
 
   if (MODE == SPEC_GREEDY || MODE == SPEC_REJECT_PATH) {
     for (int t = tid + 1; t < T; t += kSelThreads) {
@@ -701,7 +884,12 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
         const int r = A.dft_row[nb + stop];
         rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
         rp.mq = sh.m_q[stop];
-        pass_normalisers(rp, true, sy, sh, V);
+        if (A.cache) {
+          cache_load(rc, rp, true, true, sy, sh);
+          cached = true;
+        } else {
+          pass_normalisers(rp, true, sy, sh, V);
+        }
         draw_k = 0;
       }
     }
@@ -711,6 +899,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     for (;;) {
       int k = 0;
       draw_k = -1;
+      cached = false;
       bool dead = false, have_norm = false, moved = false;
       rp.lp = A.tgt + (nb + s) * V;
       rp.mp = sh.m_p[s];
@@ -746,22 +935,28 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
           break;
         }
         if (tid == 0) sh.dec[ch] = 0;
+        if (!have_norm) {
+          if (A.cache) {
+            cache_load(rc, rp, true, true, sy, sh);
+            cached = true;
+          } else {
+            pass_normalisers(rp, true, sy, sh, V);
+          }
+          have_norm = true;
+        }
         if (remaining == 0) {
           // last child rejected: the draw uses max(0, r_k - q) unnormalised
-          if (!have_norm) pass_normalisers(rp, true, sy, sh, V);
           draw_k = k;
           break;
         }
-        if (!have_norm) {
-          pass_normalisers(rp, true, sy, sh, V);
-          have_norm = true;
-        }
-        const double N = pass_residual_mass(rp, k, invN, sy, sh, V);
+        const double N =
+            A.cache ? cache_residual_mass(rc, sy, sh) : pass_residual_mass(rp, k, invN, sy, sh, V);
         if (!(N > 0.0) || k >= 63) {
           dead = true;
           if (tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
         } else {
           if (tid == 0) sh.invN[k] = 1.0 / N;
+          if (A.cache) cache_residual_step(rc, 1.0 / N);
           __syncthreads();
           ++k;
         }
@@ -787,7 +982,15 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     const double u = (double)A.u_final[b];
     double total = 0.0;
     int tok = 0, near = 0;
-    bool found = pass_draw(rp, draw_k, invN, u, sy, sh, V, &tok, &near, &total);
+    bool found;
+    if (A.cache && draw_k >= 0 && cached) {
+      found = cache_draw(rc, true, u, sy, sh, V, &tok, &near, &total);
+    } else if (A.cache && draw_k < 0) {
+      cache_load(rc, rp, false, false, sy, sh);
+      found = cache_draw(rc, false, u, sy, sh, V, &tok, &near, &total);
+    } else {
+      found = pass_draw(rp, draw_k, invN, u, sy, sh, V, &tok, &near, &total);
+    }
     if (!(total > 0.0) && draw_k >= 0) {
       // nothing left in the residual (rounding only): draw from p_stop
       if (lead && tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
@@ -919,6 +1122,10 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   A.Rr = Rr;
   A.n_chunks = pl.n_chunks;
   A.P = choose_p(mode, B, V);
+  {
+    const int slice = (V + A.P - 1) / A.P;
+    A.cache = (slice + kSelThreads - 1) / kSelThreads <= kCacheE ? 1 : 0;
+  }
   A.tgt = tgt;
   A.dft = dft;
   A.dft_row = dft_row;
