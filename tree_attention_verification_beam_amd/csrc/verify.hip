@@ -19,9 +19,11 @@
 //             own token (fp64 exp), run the mode's tests and the path select,
 //             and do the residual passes and the inverse-CDF draw over the stop
 //             row pair in fp64.  With P > 1 the workgroups of a sequence split
-//             the vocabulary, publish per-pass partial sums and meet at a
-//             counter barrier (re-armed by k_vstats); every workgroup then
-//             holds the same totals and takes the same decisions.  Such
+//             the vocabulary and exchange per-pass partial sums through
+//             tagged slots (cleared by k_vstats): every 64-bit slot word holds
+//             one 32-bit half of a value beside the exchange's round number,
+//             so a reader needs no separate arrival count.  Every workgroup
+//             then holds the same totals and takes the same decisions.  Such
 //             launches are cooperative, so all workgroups are resident; every
 //             wait is bounded.
 #include "common.hpp"
@@ -34,7 +36,8 @@ constexpr int kSelThreads = 256;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kMaxP = 32;
 constexpr int kMergeEntries = 1024;  // chunk partials staged in LDS per merge batch
-constexpr size_t kSyncStride = 2048;  // bytes of sync area per sequence
+constexpr int kSyncWords = 2 * kMaxP * 4;  // [2 parities][kMaxP][4 tagged halves]
+constexpr size_t kSyncStride = kSyncWords * 8;  // bytes of sync area per sequence
 constexpr double kNearTie = 1e-5;
 constexpr double kCdfNearTie = 1e-9;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -148,10 +151,11 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
   if (unit < n_tgt) {
     const int b = (int)(unit / T_cap), t = (int)(unit - (long)b * T_cap);
     if (t > 0 && t >= n_nodes[b]) return;
-    // the sequence's root row, first chunk: re-arm the select's meeting counter
-    if (t == 0 && c == 0 && tid == 0)
-      __hip_atomic_store(reinterpret_cast<int*>(sync + (size_t)b * kSyncStride), 0,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the sequence's root row, first chunk: clear the select's exchange slots
+    // (round tags start again at one)
+    if (t == 0 && c == 0)
+      for (int i = tid; i < kSyncWords; i += kStatThreads)
+        store_coherent(reinterpret_cast<uint64_t*>(sync + (size_t)b * kSyncStride) + i, 0);
     row = tgt + unit * (long)V;
   } else {
     // a draft row is needed iff it is the draft row of some node with a child
@@ -291,20 +295,17 @@ struct SelShared {
 
 // Cross-workgroup meeting point of the P workgroups of one sequence.
 struct SeqSync {
-  int* counter;
-  double* slot;  // [2 parities][kMaxP][2]
+  uint64_t* slot;  // [2 parities][kMaxP][4]: low/high halves of a, then of b
   int P, w, rounds;
   int32_t* status;
 
-  __device__ void publish(double a, double b) {
-    // called by thread 0 only
-    double* s = slot + ((rounds & 1) * kMaxP + w) * 2;
-    __hip_atomic_store(s, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(s + 1, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
   // Everyone publishes (a, b), waits for the other workgroups and returns the
-  // per-workgroup values in s_slots (identical in every workgroup).
+  // per-workgroup values in s_slots (identical in every workgroup).  Word k of
+  // a workgroup's slot holds 32 bits of its values in the low half and the
+  // round number plus one in the high half: a word read at the coherent level
+  // with the current tag is this round's, whatever order the stores landed in.
+  // Round r + 2 reuses round r's parity only after every workgroup has
+  // published round r + 1, i.e. after every reader is done with round r.
   __device__ void exchange(double a, double b, double* s_slots) {
     if (P == 1) {
       if (threadIdx.x == 0) {
@@ -316,24 +317,38 @@ struct SeqSync {
       return;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      // slots are written and read at the coherent level; the count follows
-      // the completed slot stores
-      publish(a, b);
-      wait_stores_done();
-      __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const int target = P * (rounds + 1);
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const uint32_t tag = (uint32_t)rounds + 1u;
+      uint64_t* base = slot + (size_t)(rounds & 1) * kMaxP * 4;
+      if (lane < 4) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(lane < 2 ? a : b);
+        const uint32_t half = (lane & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
+        store_coherent(base + w * 4 + lane, ((uint64_t)tag << 32) | half);
+      }
+      // the 4P words of this parity, two per lane
+      const int n = 4 * P;
+      uint64_t v0 = 0, v1 = 0;
+      bool ok0 = lane >= n, ok1 = lane + 64 >= n;
       int spins = 0;
-      while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-        __builtin_amdgcn_s_sleep(1);
-        if (++spins > (1 << 24)) {
+      while (!(ok0 && ok1)) {
+        if (!ok0) {
+          v0 = load_coherent(base + lane);
+          ok0 = (uint32_t)(v0 >> 32) == tag;
+        }
+        if (!ok1) {
+          v1 = load_coherent(base + lane + 64);
+          ok1 = (uint32_t)(v1 >> 32) == tag;
+        }
+        if (++spins > (1 << 22)) {
           raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
           break;
         }
       }
-      const double* src = slot + (rounds & 1) * kMaxP * 2;
-      for (int i = 0; i < 2 * P; ++i)
-        s_slots[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // word k is 32-bit element k of the little-endian double array
+      uint32_t* dst = reinterpret_cast<uint32_t*>(s_slots);
+      if (lane < n) dst[lane] = (uint32_t)v0;
+      if (lane + 64 < n) dst[lane + 64] = (uint32_t)v1;
     }
     __syncthreads();
     ++rounds;
@@ -702,8 +717,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   const int tid = threadIdx.x;
   const int T_cap = A.T_cap, V = A.V;
   SeqSync sy;
-  sy.counter = reinterpret_cast<int*>(A.sync + (size_t)b * kSyncStride);
-  sy.slot = reinterpret_cast<double*>(A.sync + (size_t)b * kSyncStride + 64);
+  sy.slot = reinterpret_cast<uint64_t*>(A.sync + (size_t)b * kSyncStride);
   sy.P = A.P;
   sy.w = w;
   sy.rounds = 0;
