@@ -7,7 +7,8 @@
 - a star tree (every candidate a child of the root) in all modes;
 - a context that overflows the launch bound: that sequence gets zero rows and
   the device status bit, the others stay exact;
-- B = 0 calls (host-only, in test_abi.py).
+- B = 0 calls (host-only, in test_abi.py);
+- one attention call launched forty times, each checked (intermittent errors).
 Bar as in test_gpu_parity.py.
 """
 import numpy as np
@@ -128,3 +129,24 @@ def test_large_batch_large_vocab(gpu):
         res = step.run()
         assert res["status"] == 0, gpu.decode_status(res["status"])
         assert_verify_equal(res, oracle_verify(inp, tr, mode), f"B=64 V=1e5 {mode}")
+
+
+def test_attention_repeated_launches_match(gpu):
+    """Forty launches of one attention call whose plan has two query tiles per
+    wave, two tiles of loads in flight and two-tile context splits (the tree
+    keys fall in the first tile of the last split).  Every launch must match
+    the oracle: a wrongly unmasked tree key shows up as an intermittent error,
+    so one launch is not enough."""
+    inp = synth.make_inputs(4, 100, B_override=1, ctx_override=3000)
+    log("case repeated attention launches, B=1 ctx=3000 G=4")
+    tr = oracle_tree(inp)
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    step = pipeline.Step(inp, "greedy")
+    step.build_tree()
+    for rep in range(40):
+        step.out.fill_(float("nan"))
+        step.attention()
+        torch.cuda.synchronize()
+        assert int(step.status.item()) == 0
+        attn_bar(step.out.float().cpu().numpy(), ref, f"launch {rep}")

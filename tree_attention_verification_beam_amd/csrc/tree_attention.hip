@@ -181,25 +181,100 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   const int l16 = lane & 15;
   const int lg = lane >> 4;
 
+  // Everything this workgroup reads before its first tile is issued here, in
+  // one round trip: the sequence's lengths, the Q fragments and ancestor words
+  // of its rows (row indices clamped into the tensors; rows that turn out dead
+  // are zeroed below) and the first key tile (clamped into the cache; keys past
+  // the range are zeroed before they reach LDS).
   const int ctx = a.ctx_len[b];
   const int T = a.n_nodes[b];
+  const bf16_t* kbase = a.kc + (size_t)bh * a.cache_cap * D;
+  const bf16_t* vbase = a.vc + (size_t)bh * a.cache_cap * D;
+  const int k_begin = sp * a.tiles_per_split * kKeyTile;
+
+  // ---------------------------------------------------------------- tile loader
+  // K: 64 keys x D, unit = (key, 8-wide d octet); V: unit = (VK keys, d octet),
+  // sized so every thread owns exactly one V unit.  Key indices are clamped to
+  // `last`: the loads never branch (a full and a partial tile run the same
+  // code, so prefetched loads stay in flight), and the keys past the range are
+  // masked to -inf before the softmax, so their stand-in values get zero weight.
+  // PF register sets keep PF tiles in flight.
+  constexpr int OCT = D / 8;
+  constexpr int K_TOTAL = kKeyTile * OCT;                          // 16-byte K units per tile
+  constexpr int K_UNITS = K_TOTAL / kThreads;                      // per thread
+  constexpr int VK = kKeyTile * OCT / kThreads;                    // keys per V unit
+  static_assert(K_TOTAL % kThreads == 0 && VK >= 1 && VK <= 4, "tile split");
+
+  auto load_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0, int last) {
+#pragma unroll
+    for (int u = 0; u < K_UNITS; ++u) {
+      const int unit = tid + u * kThreads;
+      const int key = unit / OCT, oc = unit - (unit / OCT) * OCT;
+      const int kidx = min(kt0 + key, last);
+      kr[u] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kidx * D + oc * 8);
+    }
+    const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
+#pragma unroll
+    for (int j = 0; j < VK; ++j) {
+      const int kidx = min(kt0 + VK * kq + j, last);
+      vr[j] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kidx * D + oc * 8);
+    }
+  };
+  // zero the keys of a speculatively loaded tile that lie past `last` (cache
+  // slots past the sequence may hold any bits, NaN included)
+  auto sanitize_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0, int last) {
+#pragma unroll
+    for (int u = 0; u < K_UNITS; ++u) {
+      const int key = (tid + u * kThreads) / OCT;
+      if (kt0 + key > last) kr[u] = bf16x8{};
+    }
+    const int kq = tid / OCT;
+#pragma unroll
+    for (int j = 0; j < VK; ++j)
+      if (kt0 + VK * kq + j > last) vr[j] = bf16x8{};
+  };
+
+  bf16x8 kA[K_UNITS], vA[VK];
+  load_tile(kA, vA, k_begin, a.cache_cap - 1);
+
+  // Q fragments: B operand of S^T = K Q^T; lane (query l16, group lg) holds
+  // Q[row][32s + 8lg .. +8]
+  int qt_idx[QT];
+  bf16x8 qf[QT][KSTEPS];
+  uint64_t mask0[QT], mask1[QT];
+#pragma unroll
+  for (int i = 0; i < QT; ++i) {
+    qt_idx[i] = mt * RG * QT + i * RG + rg;
+    const int r = min(qt_idx[i] * 16 + l16, M_cap - 1);
+    const int t = r / G;
+    const int gq = r - t * G;
+    const bf16_t* qrow = a.q + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[i][s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg);
+    mask0[i] = a.anc[((size_t)b * T_cap + t) * n_words];
+    mask1[i] = n_words > 1 ? a.anc[((size_t)b * T_cap + t) * n_words + 1] : 0ull;
+  }
+
   const bool bad =
       T < 1 || T > T_cap || ctx < 0 || ctx > a.max_ctx || ctx + T > a.cache_cap;
   const int rows_valid = bad ? 0 : G * T;
   const int nq_valid = (rows_valid + 15) >> 4;
   const int n_keys = ctx + T;
-  const int k_begin = sp * a.tiles_per_split * kKeyTile;
   int k_end = k_begin + a.tiles_per_split * kKeyTile;
   if (k_end > n_keys) k_end = n_keys;
   if (bad && sp == 0 && mt == 0 && tid == 0) raise_status(a.status, SPEC_DEV_CTX_RANGE);
 
   // this wave's query tiles: interleaved over the row groups of the workgroup
-  int qt_idx[QT];
   bool qt_on[QT];
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
-    qt_idx[i] = mt * RG * QT + i * RG + rg;
     qt_on[i] = qt_idx[i] < nq_valid && k_begin < k_end;
+    const int r = qt_idx[i] * 16 + l16;
+    const bool live = qt_on[i] && r < rows_valid;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) qf[i][s] = live ? qf[i][s] : bf16x8{};
+    mask0[i] = live ? mask0[i] : 0ull;
+    mask1[i] = live ? mask1[i] : 0ull;
   }
   const int wg_first_row = mt * RG * QT * 16;
   const int wg_end_row = min(M_cap, wg_first_row + RG * QT * 16);
@@ -223,29 +298,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     }
     return;
   }
-
-  // ---------------------------------------------------------------- Q fragments
-  // B operand of S^T = K Q^T: lane (query l16, group lg) holds Q[row][32s + 8lg .. +8]
-  bf16x8 qf[QT][KSTEPS];
-  uint64_t mask0[QT], mask1[QT];
-#pragma unroll
-  for (int i = 0; i < QT; ++i) {
-    const int r = qt_idx[i] * 16 + l16;
-    const int t = r / G;
-    const int gq = r - t * G;
-    const bool live = qt_on[i] && r < rows_valid;
-    const bf16_t* qrow = a.q + (((size_t)b * T_cap + t) * H + g_kv * G + gq) * D;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s) {
-      if (live) {
-        qf[i][s] = *reinterpret_cast<const bf16x8*>(qrow + 32 * s + 8 * lg);
-      } else {
-        qf[i][s] = bf16x8{};
-      }
-    }
-    mask0[i] = live ? a.anc[((size_t)b * T_cap + t) * n_words] : 0ull;
-    mask1[i] = (live && n_words > 1) ? a.anc[((size_t)b * T_cap + t) * n_words + 1] : 0ull;
-  }
+  const int klast = k_end - 1;
+  sanitize_tile(kA, vA, k_begin, klast);
 
   // ---------------------------------------------------------------- state
   f32x4 acc[QT][DT];
@@ -258,38 +312,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     for (int d = 0; d < DT; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const bf16_t* kbase = a.kc + (size_t)bh * a.cache_cap * D;
-  const bf16_t* vbase = a.vc + (size_t)bh * a.cache_cap * D;
-
-  // ---------------------------------------------------------------- tile loader
-  // K: 64 keys x D, unit = (key, 8-wide d octet); V: unit = (VK keys, d octet),
-  // sized so every thread owns exactly one V unit.  Key indices are clamped to
-  // the last key of the range: the loads never branch (a full and a partial
-  // tile run the same code, so prefetched loads stay in flight), and the keys
-  // past the range are masked to -inf before the softmax, so their finite
-  // stand-in values get zero weight.  PF register sets keep PF tiles in flight.
-  constexpr int OCT = D / 8;
-  constexpr int K_TOTAL = kKeyTile * OCT;                          // 16-byte K units per tile
-  constexpr int K_UNITS = K_TOTAL / kThreads;                      // per thread
-  constexpr int VK = kKeyTile * OCT / kThreads;                    // keys per V unit
-  static_assert(K_TOTAL % kThreads == 0 && VK >= 1 && VK <= 4, "tile split");
-  const int klast = k_end - 1;
-
-  auto load_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0) {
-#pragma unroll
-    for (int u = 0; u < K_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int key = unit / OCT, oc = unit - (unit / OCT) * OCT;
-      const int kidx = min(kt0 + key, klast);
-      kr[u] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kidx * D + oc * 8);
-    }
-    const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
-#pragma unroll
-    for (int j = 0; j < VK; ++j) {
-      const int kidx = min(kt0 + VK * kq + j, klast);
-      vr[j] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kidx * D + oc * 8);
-    }
-  };
   auto store_tile = [&](const bf16x8 (&kr)[K_UNITS], const bf16x8 (&vr)[VK], int stage) {
     bf16_t* sk = smem + stage * Lds<D>::kStage;
     bf16_t* sv = sk + Lds<D>::kStageK;
@@ -320,10 +342,39 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // One 64-key tile from LDS stage `stage` (first key kt0).  Each 32-key chunk of
   // this wave's keys: S^T = K Q^T (two 16-key sub-tiles), online softmax, then
   // O^T += V^T P^T with the chunk as one 32-key k-step.
+  // Visibility of the 64 keys of the tile at kt0 for query tile i of this lane,
+  // bit p <-> key kt0 + p: context keys before ctx, tree keys whose ancestor bit
+  // is set, and nothing at or past k_end.  All shift amounts are uniform.
+  auto tile_vis = [&](int i, int kt0) -> uint64_t {
+    const int nctx = ctx - kt0;  // tile keys before the tree
+    uint64_t bits;
+    if (nctx >= kKeyTile) {
+      bits = ~0ull;
+    } else if (nctx >= 0) {
+      bits = (nctx > 0 ? (~0ull >> (64 - nctx)) : 0ull) | (mask0[i] << nctx);
+    } else {
+      const int sh = -nctx;  // tree index of the tile's first key
+      bits = sh >= 128 ? 0ull
+             : sh >= 64 ? (mask1[i] >> (sh - 64))
+             : sh == 0  ? mask0[i]
+                        : (mask0[i] >> sh) | (mask1[i] << (64 - sh));
+    }
+    const int nin = k_end - kt0;  // tile keys inside the range
+    if (nin < kKeyTile) bits &= nin > 0 ? (~0ull >> (64 - nin)) : 0ull;
+    return bits;
+  };
+
   auto compute_tile = [&](int stage, int kt0) {
     const bf16_t* sk = smem + stage * Lds<D>::kStage;
     const bf16_t* sv = sk + Lds<D>::kStageK;
     const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
+    // this lane's keys of the tile start at wkey0 + 4 lg; bit c of lvis[i] is
+    // the key at wkey0 + 4 lg + c
+    uint64_t lvis[QT];
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < QT; ++i) lvis[i] = tile_vis(i, kt0) >> (wkey0 + 4 * lg);
+    }
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
       const int ck0 = wkey0 + 32 * j;  // first key of the chunk inside the tile
@@ -353,11 +404,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           for (int st = 0; st < 2; ++st) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int key = kt0 + ck0 + 16 * st + 4 * lg + e;
-              const int aa = key - ctx;
-              const uint64_t w = aa < 64 ? mask0[i] : mask1[i];
-              const bool tree_vis = ((w >> (aa & 63)) & 1ull) != 0ull;
-              const bool vis = key < k_end && (aa < 0 || tree_vis);
+              const int c = 32 * j + 16 * st + e;  // compile-time bit position
+              const uint32_t word = c < 32 ? (uint32_t)lvis[i] : (uint32_t)(lvis[i] >> 32);
+              const bool vis = (word >> (c & 31)) & 1u;
               sacc[i][st][e] = vis ? sacc[i][st][e] : -INFINITY;
             }
           }
@@ -420,8 +469,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // LDS double buffer; PF tiles of global loads in flight.  The barrier waits
   // for this wave's LDS traffic only, so prefetched global loads stay in flight.
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
-  bf16x8 kA[K_UNITS], vA[VK];
-  load_tile(kA, vA, k_begin);
   if constexpr (PF == 1) {
     store_tile(kA, vA, 0);
     lds_barrier();
@@ -429,7 +476,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     for (int it = 0; it < n_tiles; ++it) {
       const int kt0 = k_begin + it * kKeyTile;
       const bool more = it + 1 < n_tiles;
-      if (more) load_tile(kA, vA, kt0 + kKeyTile);
+      if (more) load_tile(kA, vA, kt0 + kKeyTile, klast);
       compute_tile(it & 1, kt0);
       if (more) store_tile(kA, vA, (it + 1) & 1);
       lds_barrier();
@@ -440,18 +487,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     // loads past the end fetch a resident row) and the loop body is straight
     // line, so the loads of the next two tiles stay in flight across barriers.
     bf16x8 kB[K_UNITS], vB[VK];
-    load_tile(kB, vB, k_begin + kKeyTile);
+    load_tile(kB, vB, k_begin + kKeyTile, klast);
     store_tile(kA, vA, 0);
     lds_barrier();
     const int n_pairs = (n_tiles + 1) >> 1;
 #pragma unroll 1
     for (int it = 0; it < n_pairs; ++it) {
       const int kt0 = k_begin + 2 * it * kKeyTile;  // tile 2it in stage 0, 2it+1 in B
-      load_tile(kA, vA, kt0 + 2 * kKeyTile);
+      load_tile(kA, vA, kt0 + 2 * kKeyTile, klast);
       compute_tile(0, kt0);
       store_tile(kB, vB, 1);
       lds_barrier();
-      load_tile(kB, vB, kt0 + 3 * kKeyTile);
+      load_tile(kB, vB, kt0 + 3 * kKeyTile, klast);
       if (2 * it + 1 < n_tiles) compute_tile(1, kt0 + kKeyTile);
       store_tile(kA, vA, 0);
       lds_barrier();
@@ -541,8 +588,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 }
 
 // Combine the per-split partials of one (b, kv head) and write bf16 rows.  A
-// thread owns one row and 4 output dims; the loads of all splits are issued
-// together (unrolled up to MAXS) so the merge runs at memory speed.
+// thread owns one row and 4 output dims.  Every load of every split is issued
+// up front and unconditionally (one memory round trip); a split that saw no
+// key for the row (m = -inf) is dropped by a select, so whatever its unwritten
+// O partial holds never reaches the sum.
 template <int D, int MAXS>
 __global__ __launch_bounds__(256) void k_attn_merge(int T_cap, int H, int Hkv, int cache_cap,
                                                     int max_ctx, int n_splits,
@@ -561,30 +610,34 @@ __global__ __launch_bounds__(256) void k_attn_merge(int T_cap, int H, int Hkv, i
   const int r = blockIdx.x * RPB + threadIdx.x / TPR;
   const int d0 = 4 * (threadIdx.x % TPR);
   if (r >= M_cap) return;
+  float ms[MAXS], ls[MAXS];
+  f32x4 os[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const int sc = s < n_splits ? s : n_splits - 1;  // in-bounds stand-in, dropped below
+    const size_t u = (size_t)bh * n_splits + sc;
+    ms[s] = part_m[u * M_cap + r];
+    ls[s] = part_l[u * M_cap + r];
+    os[s] = *reinterpret_cast<const f32x4*>(part_o + (u * M_cap + r) * D + d0);
+  }
   const int ctx = ctx_len[b], T = n_nodes[b];
   const bool bad = T < 1 || T > T_cap || ctx < 0 || ctx > max_ctx || ctx + T > cache_cap;
   const int rows_valid = bad ? 0 : G * T;
   const int t = r / G, gq = r - t * G;
+  float M = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s)
+    if (s < n_splits) M = fmaxf(M, ms[s]);
   f32x4 o{0.f, 0.f, 0.f, 0.f};
-  if (r < rows_valid) {
-    float ms[MAXS];
-    float M = -INFINITY;
+  float L = 0.0f;
+  if (r < rows_valid && M != -INFINITY) {
 #pragma unroll
     for (int s = 0; s < MAXS; ++s) {
-      ms[s] = s < n_splits ? part_m[((size_t)bh * n_splits + s) * M_cap + r] : -INFINITY;
-      M = fmaxf(M, ms[s]);
-    }
-    float L = 0.0f;
-    if (M != -INFINITY) {
+      const bool use = s < n_splits && ms[s] != -INFINITY;
+      const float w = use ? __builtin_amdgcn_exp2f(ms[s] - M) : 0.0f;
+      L += use ? ls[s] * w : 0.0f;
 #pragma unroll
-      for (int s = 0; s < MAXS; ++s) {
-        if (ms[s] == -INFINITY) continue;
-        const size_t u = (size_t)bh * n_splits + s;
-        const float w = __builtin_amdgcn_exp2f(ms[s] - M);
-        L += part_l[u * M_cap + r] * w;
-        const f32x4 po = *reinterpret_cast<const f32x4*>(part_o + (u * M_cap + r) * D + d0);
-        o += po * w;
-      }
+      for (int e = 0; e < 4; ++e) o[e] += use ? os[s][e] * w : 0.0f;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     o *= inv;
@@ -692,7 +745,6 @@ int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   SPEC_ATTN_CASE(4, 1, 2, 2)
   SPEC_ATTN_CASE(4, 2, 2, 2)
   SPEC_ATTN_CASE(4, 1, 1, 2)
-  SPEC_ATTN_CASE(4, 2, 1, 2)
   SPEC_ATTN_CASE(8, 1, 2, 2)
   SPEC_ATTN_CASE(8, 1, 1, 2)
   SPEC_ATTN_CASE(8, 2, 1, 2)
