@@ -10,6 +10,10 @@
 // order, and every node writes its parent, depth and ancestor mask.
 //
 // One workgroup of SPEC_MAX_TREE threads per sequence; everything lives in LDS.
+// The prefix test is split in two data-parallel passes so that no thread walks
+// a chain of dependent LDS reads: first every candidate pair (i2 < i) finds the
+// first position where the two differ, then token (i, k) takes the smallest i2
+// whose first difference lies past k.  The scan is two wave ballots.
 #include "common.hpp"
 
 namespace spec {
@@ -17,18 +21,21 @@ namespace {
 
 constexpr int kThreads = SPEC_MAX_TREE;
 
-// Inclusive scan over the block (kThreads values), in LDS.
-__device__ int block_inclusive_scan(int v, int* s_buf) {
-  const int tid = threadIdx.x;
-  s_buf[tid] = v;
+static_assert(kThreads == 2 * kWave, "the scan below covers two waves");
+
+// Inclusive scan of a 0/1 flag over the block's two waves.  Returns the
+// inclusive count for this thread and the block total in *total.
+__device__ int block_flag_scan(int flag, int* s_wave, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const uint64_t bal = __ballot(flag);
+  const uint64_t upto = lane == kWave - 1 ? ~0ull : ((1ull << (lane + 1)) - 1ull);
+  int incl = __popcll(bal & upto);
+  if (lane == 0) s_wave[wave] = __popcll(bal);
   __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    int add = tid >= off ? s_buf[tid - off] : 0;
-    __syncthreads();
-    s_buf[tid] += add;
-    __syncthreads();
-  }
-  return s_buf[tid];
+  if (wave == 1) incl += s_wave[0];
+  *total = s_wave[0] + s_wave[1];
+  return incl;
 }
 
 // Writes node t's row (parent, token, depth, mask) given the node's parent
@@ -63,33 +70,43 @@ __global__ __launch_bounds__(kThreads) void k_build_beams(
     int32_t* __restrict__ parent, int32_t* __restrict__ token, int32_t* __restrict__ depth,
     uint64_t* __restrict__ anc, int32_t* __restrict__ beam_node) {
   __shared__ int s_cand[kThreads];  // candidate tokens, beam-major
-  __shared__ int s_scan[kThreads];
+  __shared__ int s_wave[2];
   __shared__ int s_node[kThreads];  // node id of every (i, k)
   __shared__ int s_par[kThreads];   // per node
   __shared__ int s_tok[kThreads];
+  // first differing position of candidates i2 < i, at [i2 * W + i] (W * W <= 127^2)
+  __shared__ unsigned char s_fm[(kThreads - 1) * (kThreads - 1)];
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int n = W * L;
   const int n_words = (T_cap + 63) / 64;
   const size_t base = (size_t)b * n;
+  const int root = tid == 0 ? root_token[b] : 0;  // in flight with the candidates
   if (tid < n) s_cand[tid] = beams[base + tid];
   __syncthreads();
 
-  // smallest candidate sharing this candidate's prefix of length k+1
+  // pass 1: first position where candidates i2 < i differ (L if they never do);
+  // every compare is independent, so the LDS reads pipeline
+  for (int p = tid; p < W * W; p += kThreads) {
+    const int i2 = p / W, i1 = p - (p / W) * W;
+    if (i2 >= i1) continue;
+    int fm = L;
+    for (int j = L - 1; j >= 0; --j)
+      if (s_cand[i2 * L + j] != s_cand[i1 * L + j]) fm = j;
+    s_fm[p] = (unsigned char)fm;
+  }
+  __syncthreads();
+
+  // pass 2: the smallest candidate sharing token (i, k)'s prefix of length k+1
   const int i = tid / L, k = tid - (tid / L) * L;
   int src = i;
   if (tid < n) {
-    for (int i2 = 0; i2 < i; ++i2) {
-      bool same = true;
-      for (int j = 0; j <= k; ++j)
-        if (s_cand[i2 * L + j] != s_cand[i * L + j]) { same = false; break; }
-      if (same) { src = i2; break; }
-    }
+    for (int i2 = i - 1; i2 >= 0; --i2)
+      if (s_fm[i2 * W + i] > k) src = i2;
   }
   const int is_new = (tid < n && src == i) ? 1 : 0;
-  const int incl = block_inclusive_scan(is_new, s_scan);
-  const int total_new = s_scan[kThreads - 1];
-  __syncthreads();
+  int total_new;
+  const int incl = block_flag_scan(is_new, s_wave, &total_new);
   // first appearances get ids 1, 2, ... in beam-major order
   if (is_new) s_node[tid] = incl;
   __syncthreads();
@@ -100,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void k_build_beams(
   const int T = 1 + total_new;
   if (tid == 0) {
     s_par[0] = -1;
-    s_tok[0] = root_token[b];
+    s_tok[0] = root;
   }
   if (is_new) {
     const int id = s_node[tid];
@@ -127,17 +144,20 @@ __global__ __launch_bounds__(kThreads) void k_build_explicit(
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int n_words = (T_cap + 63) / 64;
+  // all global reads in one round trip
+  const int root = tid == 0 ? root_token[b] : 0;
+  const int p = tid < N ? cand_parent[(size_t)b * N + tid] : 0;
+  const int tok = tid < N ? cand_token[(size_t)b * N + tid] : 0;
   if (tid == 0) {
     s_bad = 0;
     s_par[0] = -1;
-    s_tok[0] = root_token[b];
+    s_tok[0] = root;
   }
   __syncthreads();
   if (tid < N) {
-    const int p = cand_parent[(size_t)b * N + tid];
     if (p < 0 || p > tid) atomicOr(&s_bad, 1);
     s_par[tid + 1] = p;
-    s_tok[tid + 1] = cand_token[(size_t)b * N + tid];
+    s_tok[tid + 1] = tok;
   }
   __syncthreads();
   const int T = s_bad ? 1 : N + 1;

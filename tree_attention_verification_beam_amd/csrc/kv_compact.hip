@@ -28,12 +28,16 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
   extern __shared__ __align__(16) unsigned char buf[];  // [T_cap - 1][row bytes]
   __shared__ int s_src[SPEC_MAX_TREE];
   __shared__ int s_ok, s_ctx, s_last;
+  static_assert(kThreads >= SPEC_MAX_TREE, "one path entry per thread");
   const int b = blockIdx.x;
   const int g = blockIdx.y >> 1;
   const int which = blockIdx.y & 1;
   const int tid = threadIdx.x;
   const int n = acc_len[b];
   const int32_t* path = acc_path + (size_t)b * T_cap;
+  // the whole path row is read with the length and the arrival count, in one
+  // round trip; entries past the accepted length are ignored
+  const int my_src = tid < T_cap ? path[tid] : 0;
   if (tid == 0) {
     const int old = atomicAdd(ctx_len + b, kArrive);
     const int ctx = old & (kArrive - 1);
@@ -41,15 +45,13 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
     s_last = (old >> 24) == 2 * Hkv - 1;
     s_ok = (n >= 0 && n < T_cap && ctx + n + 1 <= cache_cap) ? 1 : 0;
   }
+  if (tid < T_cap) s_src[tid] = my_src;
   __syncthreads();
   const int ctx = s_ctx;
-  if (s_ok) {
-    for (int i = 1 + tid; i <= n; i += kThreads) {
-      const int src = path[i];
-      // node ids along a path increase strictly and are at least their depth
-      if (src < i || ctx + src >= cache_cap || (i > 1 && src <= path[i - 1])) atomicAnd(&s_ok, 0);
-      s_src[i] = src;
-    }
+  if (s_ok && tid >= 1 && tid <= n) {
+    // node ids along a path increase strictly and are at least their depth
+    if (my_src < tid || ctx + my_src >= cache_cap || (tid > 1 && my_src <= s_src[tid - 1]))
+      atomicAnd(&s_ok, 0);
   }
   __syncthreads();
   if (s_ok) {

@@ -614,11 +614,15 @@ __global__ __launch_bounds__(256) void k_attn_merge(int T_cap, int H, int Hkv, i
   f32x4 os[MAXS];
 #pragma unroll
   for (int s = 0; s < MAXS; ++s) {
-    const int sc = s < n_splits ? s : n_splits - 1;  // in-bounds stand-in, dropped below
-    const size_t u = (size_t)bh * n_splits + sc;
-    ms[s] = part_m[u * M_cap + r];
-    ls[s] = part_l[u * M_cap + r];
-    os[s] = *reinterpret_cast<const f32x4*>(part_o + (u * M_cap + r) * D + d0);
+    ms[s] = -INFINITY;
+    ls[s] = 0.0f;
+    os[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (s < n_splits) {  // uniform
+      const size_t u = (size_t)bh * n_splits + s;
+      ms[s] = part_m[u * M_cap + r];
+      ls[s] = part_l[u * M_cap + r];
+      os[s] = *reinterpret_cast<const f32x4*>(part_o + (u * M_cap + r) * D + d0);
+    }
   }
   const int ctx = ctx_len[b], T = n_nodes[b];
   const bool bad = T < 1 || T > T_cap || ctx < 0 || ctx > max_ctx || ctx + T > cache_cap;
@@ -764,6 +768,7 @@ int launch_merge(const AttnPlan& p, const AttnArgs& a, hipStream_t s) {
                        a.part_m, a.part_l, a.out);                                             \
     return launch_status();                                                                    \
   }
+  SPEC_MERGE_CASE(2)
   SPEC_MERGE_CASE(4)
   SPEC_MERGE_CASE(8)
   SPEC_MERGE_CASE(16)
