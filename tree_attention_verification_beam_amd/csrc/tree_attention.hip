@@ -106,6 +106,13 @@ template <int D>
 struct Lds {
   static constexpr int kPitchK = D + 8;         // bf16 elements per K row
   static constexpr int kPitchV = kKeyTile + 4;  // bf16 elements per transposed V row
+  // Transposed V row r holds key k at column k ^ swz(r), a multiple of 4 that
+  // is constant over each 16-row operand tile, so a read of 4 aligned keys
+  // stays contiguous and costs no per-lane address work.  It spreads the
+  // stores of one wave (16 rows x 4 key groups) over distinct banks; without
+  // it they were 4- to 8-way conflicts.  (A per-lane variant that is also
+  // conflict-free for 64-bank reads needs ~35 more VGPRs and measured slower.)
+  static __device__ constexpr int swz(int row) { return ((row >> 4) & 7) * 4; }
   static constexpr int kStageK = kKeyTile * kPitchK;
   static constexpr int kStageV = D * kPitchV;
   static constexpr int kStage = kStageK + kStageV;
@@ -324,7 +331,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      bf16_t* dst = sv + (oc * 8 + e) * Lds<D>::kPitchV + VK * kq;
+      const int row = oc * 8 + e;
+      bf16_t* dst = sv + row * Lds<D>::kPitchV + ((VK * kq) ^ Lds<D>::swz(row));
       if constexpr (VK == 4) {
         *reinterpret_cast<bf16x4*>(dst) = bf16x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
       } else if constexpr (VK == 2) {
@@ -455,8 +463,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + key_a);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + key_a + 16);
+        const int sw = Lds<D>::swz(16 * d);  // the same for rows 16d .. 16d+15
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + (key_a ^ sw));
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + ((key_a + 16) ^ sw));
         const bf16x8 vf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
         for (int i = 0; i < QT; ++i)
