@@ -37,6 +37,7 @@ constexpr int kKeyTile = 64;      // keys per LDS stage
 constexpr int kNumCU = 256;       // MI355X compute units
 constexpr int kMaxSplits = 32;    // context splits per (sequence, KV head)
 constexpr float kRescale = 8.0f;  // lazy-rescale threshold (log2 units)
+constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3 for raw 32-bit-format loads (gfx9 family)
 
 // ------------------------------------------------------------------ geometry
 
@@ -89,6 +90,9 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
   const long by_len = n_tiles / 2 > 0 ? n_tiles / 2 : 1;  // at least 2 tiles per split
   if (want > by_len) want = by_len;
   finish_plan(p, B, T_cap, H, Hkv, max_ctx, (int)want);
+  // a grid of at most about two workgroups per CU runs short, latency-bound
+  // streams: keep two tiles of loads in flight there
+  if (p.KG == 2 && p.n_slots <= 2 * kNumCU) p.PF = 2;
   return p;
 }
 
@@ -102,17 +106,23 @@ size_t partial_bytes(const AttnPlan& p, int B, int T_cap, int H, int Hkv, int D)
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 
+// Key order and LDS layout of one 32-key chunk.  Row m of the S^T MFMA's
+// sub-tile st (m = 4 q + r) is the chunk key 8 q + 4 (st ^ h(q)) + r, with
+// h(q) = (q >> 1) & 1.  The lane group q of the output then holds 8 of the
+// chunk's keys, 8 q .. 8 q + 7, so its P values form one 16-byte operand read
+// of a transposed V row, provided V^T stores key k at column vcol(k) below,
+// which swaps the two 4-key halves of every 8-key block with h = 1.  The
+// permutation h, the row pitches and the row swizzle swz keep the K operand
+// reads (16 lanes x 16 bytes per phase), the V^T stores and the V^T operand
+// reads of a wave on distinct banks of a 64-bank LDS.
 template <int D>
 struct Lds {
   static constexpr int kPitchK = D + 8;         // bf16 elements per K row
-  static constexpr int kPitchV = kKeyTile + 4;  // bf16 elements per transposed V row
-  // Transposed V row r holds key k at column k ^ swz(r), a multiple of 4 that
-  // is constant over each 16-row operand tile, so a read of 4 aligned keys
-  // stays contiguous and costs no per-lane address work.  It spreads the
-  // stores of one wave (16 rows x 4 key groups) over distinct banks; without
-  // it they were 4- to 8-way conflicts.  (A per-lane variant that is also
-  // conflict-free for 64-bank reads needs ~35 more VGPRs and measured slower.)
-  static __device__ constexpr int swz(int row) { return ((row >> 4) & 7) * 4; }
+  static constexpr int kPitchV = kKeyTile + 8;  // bf16 elements per transposed V row
+  static __device__ constexpr int swz(int row) { return ((row >> 4) & 7) * 8; }
+  static __device__ constexpr int vcol(int key, int row) {
+    return key ^ (((key >> 4) & 1) * 4) ^ swz(row);
+  }
   static constexpr int kStageK = kKeyTile * kPitchK;
   static constexpr int kStageV = D * kPitchV;
   static constexpr int kStage = kStageK + kStageV;
@@ -181,7 +191,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   const int n_words = (T_cap + 63) / 64;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave choices scalar
   const int lane = tid & 63;
   const int rg = wave / KG;
   const int kg = wave - rg * KG;
@@ -201,31 +211,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 
   // ---------------------------------------------------------------- tile loader
   // K: 64 keys x D, unit = (key, 8-wide d octet); V: unit = (VK keys, d octet),
-  // sized so every thread owns exactly one V unit.  Key indices are clamped to
-  // `last`: the loads never branch (a full and a partial tile run the same
-  // code, so prefetched loads stay in flight), and the keys past the range are
-  // masked to -inf before the softmax, so their stand-in values get zero weight.
-  // PF register sets keep PF tiles in flight.
+  // sized so every thread owns exactly one V unit.  A tile is read with buffer
+  // loads through a resource that starts at the tile's first key and ends at
+  // `limit` keys: every thread's byte offset inside a tile is fixed, the
+  // resource is built with scalar ops, and the hardware range check returns
+  // zeros for keys at or past `limit`.  So the loads never branch or clamp (a
+  // full and a partial tile run the same code, and prefetched loads stay in
+  // flight), and keys past the range reach LDS as zeros, to be masked to -inf
+  // before the softmax.  PF register sets keep PF tiles in flight.
   constexpr int OCT = D / 8;
   constexpr int K_TOTAL = kKeyTile * OCT;                          // 16-byte K units per tile
   constexpr int K_UNITS = K_TOTAL / kThreads;                      // per thread
   constexpr int VK = kKeyTile * OCT / kThreads;                    // keys per V unit
   static_assert(K_TOTAL % kThreads == 0 && VK >= 1 && VK <= 4, "tile split");
+  constexpr int kRowBytes = D * 2;
 
-  auto load_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0, int last) {
+  int koff[K_UNITS], voff[VK];  // byte offsets inside a tile
 #pragma unroll
-    for (int u = 0; u < K_UNITS; ++u) {
-      const int unit = tid + u * kThreads;
-      const int key = unit / OCT, oc = unit - (unit / OCT) * OCT;
-      const int kidx = min(kt0 + key, last);
-      kr[u] = *reinterpret_cast<const bf16x8*>(kbase + (size_t)kidx * D + oc * 8);
-    }
-    const int kq = tid / OCT, oc = tid - (tid / OCT) * OCT;
+  for (int u = 0; u < K_UNITS; ++u) {
+    const int unit = tid + u * kThreads;
+    koff[u] = (unit / OCT) * kRowBytes + (unit % OCT) * 16;
+  }
 #pragma unroll
-    for (int j = 0; j < VK; ++j) {
-      const int kidx = min(kt0 + VK * kq + j, last);
-      vr[j] = *reinterpret_cast<const bf16x8*>(vbase + (size_t)kidx * D + oc * 8);
-    }
+  for (int j = 0; j < VK; ++j) voff[j] = (VK * (tid / OCT) + j) * kRowBytes + (tid % OCT) * 16;
+
+  auto tile_rsrc = [&](const bf16_t* base, int kt0, int limit) {
+    const int rows = limit - kt0 > 0 ? limit - kt0 : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16_t*>(base + (size_t)kt0 * D), (short)0,
+                                             rows * kRowBytes, kBufferWord3);
+  };
+  auto load_tile = [&](bf16x8 (&kr)[K_UNITS], bf16x8 (&vr)[VK], int kt0, int limit) {
+    const auto rk = tile_rsrc(kbase, kt0, limit);
+    const auto rv = tile_rsrc(vbase, kt0, limit);
+#pragma unroll
+    for (int u = 0; u < K_UNITS; ++u)
+      kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
+#pragma unroll
+    for (int j = 0; j < VK; ++j)
+      vr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0));
   };
   // zero the keys of a speculatively loaded tile that lie past `last` (cache
   // slots past the sequence may hold any bits, NaN included)
@@ -242,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   };
 
   bf16x8 kA[K_UNITS], vA[VK];
-  load_tile(kA, vA, k_begin, a.cache_cap - 1);
+  load_tile(kA, vA, k_begin, a.cache_cap);  // every cache slot: sanitized below
 
   // Q fragments: B operand of S^T = K Q^T; lane (query l16, group lg) holds
   // Q[row][32s + 8lg .. +8]
@@ -283,6 +306,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     mask0[i] = live ? mask0[i] : 0ull;
     mask1[i] = live ? mask1[i] : 0ull;
   }
+  bool wave_on = false;
+#pragma unroll
+  for (int i = 0; i < QT; ++i) wave_on = wave_on || qt_on[i];
   const int wg_first_row = mt * RG * QT * 16;
   const int wg_end_row = min(M_cap, wg_first_row + RG * QT * 16);
   const bool wg_active = wg_first_row < rows_valid && k_begin < k_end;
@@ -332,7 +358,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int row = oc * 8 + e;
-      bf16_t* dst = sv + row * Lds<D>::kPitchV + ((VK * kq) ^ Lds<D>::swz(row));
+      bf16_t* dst = sv + row * Lds<D>::kPitchV + Lds<D>::vcol(VK * kq, row);
       if constexpr (VK == 4) {
         *reinterpret_cast<bf16x4*>(dst) = bf16x4{vr[0][e], vr[1][e], vr[2][e], vr[3][e]};
       } else if constexpr (VK == 2) {
@@ -375,13 +401,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   auto compute_tile = [&](int stage, int kt0) {
     const bf16_t* sk = smem + stage * Lds<D>::kStage;
     const bf16_t* sv = sk + Lds<D>::kStageK;
+    if (!wave_on) return;  // no live query tile in this wave (uniform)
     const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
-    // this lane's keys of the tile start at wkey0 + 4 lg; bit c of lvis[i] is
-    // the key at wkey0 + 4 lg + c
+    // this lane's keys of chunk j are wkey0 + 32 j + 8 lg + 4 (st ^ h) + e
+    // (h = (lg >> 1) & 1); bit 32 j + 4 st + e of lvis[i] is that key's
     uint64_t lvis[QT];
     if (need_mask) {
+      const bool h = (lg >> 1) & 1;
 #pragma unroll
-      for (int i = 0; i < QT; ++i) lvis[i] = tile_vis(i, kt0) >> (wkey0 + 4 * lg);
+      for (int i = 0; i < QT; ++i) {
+        const uint64_t v = tile_vis(i, kt0) >> (wkey0 + 8 * lg);
+        const uint64_t sw = ((v >> 4) & 0x0F0F0F0F0F0F0F0Full) | ((v << 4) & 0xF0F0F0F0F0F0F0F0ull);
+        lvis[i] = h ? sw : v;
+      }
     }
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
@@ -390,16 +422,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bf16x8 kf[KSTEPS];
-        const bf16_t* krow = sk + (ck0 + 16 * st + l16) * Lds<D>::kPitchK + 8 * lg;
+        const int q = l16 >> 2;
+        const int kk = ck0 + 8 * q + 4 * (st ^ ((q >> 1) & 1)) + (l16 & 3);  // this lane's key row
+        const bf16_t* krow = sk + kk * Lds<D>::kPitchK + 8 * lg;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
 #pragma unroll
         for (int i = 0; i < QT; ++i) {
+          // a dead tile of a live wave has zero Q: its scores are computed
+          // and discarded (its rows are never written)
           f32x4 cc{0.f, 0.f, 0.f, 0.f};
-          if (qt_on[i]) {
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) cc = mfma16x16x32(kf[s], qf[i][s], cc);
-          }
+          for (int s = 0; s < KSTEPS; ++s) cc = mfma16x16x32(kf[s], qf[i][s], cc);
           sacc[i][st] = cc;
         }
       }
@@ -412,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           for (int st = 0; st < 2; ++st) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const int c = 32 * j + 16 * st + e;  // compile-time bit position
+              const int c = 32 * j + 4 * st + e;  // compile-time bit position
               const uint32_t word = c < 32 ? (uint32_t)lvis[i] : (uint32_t)(lvis[i] >> 32);
               const bool vis = (word >> (c & 31)) & 1u;
               sacc[i][st][e] = vis ? sacc[i][st][e] : -INFINITY;
@@ -421,11 +455,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         }
       }
 
-      // online softmax in exp2 form; lane owns query l16, keys ck0 + 16*st + 4*lg + e
+      // online softmax in exp2 form; lane owns query l16, keys ck0 + 8 lg + 4 (st ^ h) + e
       bf16x8 pf[QT];
 #pragma unroll
       for (int i = 0; i < QT; ++i) {
-        if (!qt_on[i]) continue;
         float lmax = fmaxf(fmaxf(fmaxf(sacc[i][0][0], sacc[i][0][1]),
                                  fmaxf(sacc[i][0][2], sacc[i][0][3])),
                            fmaxf(fmaxf(sacc[i][1][0], sacc[i][1][1]),
@@ -458,18 +491,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         l_run[i] += psum;
       }
 
-      // O^T += V^T P^T over the chunk's 32 keys
-      const int key_a = ck0 + 4 * lg;  // keys of the first sub-tile owned by this lane group
+      // O^T += V^T P^T over the chunk's 32 keys: this lane's 8 P values are
+      // the keys ck0 + 8 lg .. + 7 in V^T column order, one 16-byte read
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
         const int sw = Lds<D>::swz(16 * d);  // the same for rows 16d .. 16d+15
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vrow + (key_a ^ sw));
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vrow + ((key_a + 16) ^ sw));
-        const bf16x8 vf{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + ((ck0 + 8 * lg) ^ sw));
 #pragma unroll
-        for (int i = 0; i < QT; ++i)
-          if (qt_on[i]) acc[i][d] = mfma16x16x32(vf, pf[i], acc[i][d]);
+        for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[i], acc[i][d]);
       }
     }
   };
@@ -485,7 +515,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     for (int it = 0; it < n_tiles; ++it) {
       const int kt0 = k_begin + it * kKeyTile;
       const bool more = it + 1 < n_tiles;
-      if (more) load_tile(kA, vA, kt0 + kKeyTile, klast);
+      if (more) load_tile(kA, vA, kt0 + kKeyTile, k_end);
       compute_tile(it & 1, kt0);
       if (more) store_tile(kA, vA, (it + 1) & 1);
       lds_barrier();
@@ -496,18 +526,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     // loads past the end fetch a resident row) and the loop body is straight
     // line, so the loads of the next two tiles stay in flight across barriers.
     bf16x8 kB[K_UNITS], vB[VK];
-    load_tile(kB, vB, k_begin + kKeyTile, klast);
+    load_tile(kB, vB, k_begin + kKeyTile, k_end);
     store_tile(kA, vA, 0);
     lds_barrier();
     const int n_pairs = (n_tiles + 1) >> 1;
 #pragma unroll 1
     for (int it = 0; it < n_pairs; ++it) {
       const int kt0 = k_begin + 2 * it * kKeyTile;  // tile 2it in stage 0, 2it+1 in B
-      load_tile(kA, vA, kt0 + 2 * kKeyTile, klast);
+      load_tile(kA, vA, kt0 + 2 * kKeyTile, k_end);
       compute_tile(0, kt0);
       store_tile(kB, vB, 1);
       lds_barrier();
-      load_tile(kB, vB, kt0 + 3 * kKeyTile, klast);
+      load_tile(kB, vB, kt0 + 3 * kKeyTile, k_end);
       if (2 * it + 1 < n_tiles) compute_tile(1, kt0 + kKeyTile);
       store_tile(kA, vA, 0);
       lds_barrier();
