@@ -127,7 +127,9 @@ int spec_build_tree(int kind, int B, int W, int L, int T_cap, const int32_t *can
  * a with anc bit a set; out = softmax(scale * q.k) v over those keys.
  *
  * dt: SPEC_F32 (q, caches and out fp32) or SPEC_BF16 (bf16; fp32 accumulation
- * and softmax).  D must be 64 or 128 for bf16, 1..256 for fp32.
+ * and softmax).  D must be 64 or 128 for bf16, 1..256 for fp32.  On the bf16
+ * path one (b, KV head) cache row block, cache_cap * D * 2 bytes, must stay
+ * below 2^31 (SPEC_ERR_UNSUPPORTED otherwise).
  * q [B][T_cap][H][D]; k_cache, v_cache [B][Hkv][cache_cap][D]: the tree's own
  * K/V already sit at slots ctx..ctx+T_b-1 (node t at ctx+t); ctx_len [B]
  * (device) with ctx_len[b] <= max_ctx (host bound used to size the launch);

@@ -75,3 +75,12 @@ def test_empty_batch_is_a_no_op(lib):
                                     None, 0, None, None) == 0
     assert cdll.spec_verify(0, 0, 17, 1000, 0, *([None] * 17), 0, None, None) == 0
     assert cdll.spec_kv_compact(1, 0, 8, 128, 1100, 17, *([None] * 5), None, None) == 0
+
+
+def test_attention_rejects_a_row_block_beyond_32_bit_ranges(lib):
+    """bf16 tile loads address one (b, KV head) cache row block through 32-bit
+    buffer ranges: cache_cap * D * 2 >= 2^31 is refused on the host."""
+    cdll = lib.load()
+    cap = (1 << 23) + 1  # * 128 * 2 bytes > 2^31
+    assert cdll.spec_tree_attention(1, 1, 17, 32, 32, 128, cap, 1024, *([16] * 6), 0.0, 16,
+                                    None, 0, None, None) == -2

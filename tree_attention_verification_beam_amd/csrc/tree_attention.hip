@@ -895,6 +895,8 @@ extern "C" int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int
   }
   if (dt != SPEC_BF16) return SPEC_ERR_INVALID;
   if (D != 64 && D != 128) return SPEC_ERR_UNSUPPORTED;
+  // tile loads address one (b, KV head) row block through 32-bit buffer ranges
+  if ((long long)cache_cap * D * 2 > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
     return SPEC_ERR_INVALID;
   const AttnPlan p = make_plan(B, T_cap, H, Hkv, max_ctx);
