@@ -81,12 +81,18 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
     // one row block: two query tiles per wave, two tiles of loads in flight
     p.KG = 1; p.QT = 2; p.PF = 2;
   } else {
-    // many rows (wide GQA groups): 128-row blocks read the same key range
-    p.KG = 1; p.QT = 1; p.PF = 1;
+    // many rows (wide GQA groups): 128-row blocks of 4 waves with two query
+    // tiles each read the same key range, two workgroups per CU
+    p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 1;
   }
   const long units = (long)B * Hkv;
   const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
-  long want = (kNumCU + units - 1) / units;
+  // enough context splits that the workgroups (units x row blocks x splits)
+  // cover every CU once, or twice for 4-wave groups
+  const int per_wg = p.NW / p.KG * p.QT;
+  const long n_mt = (nq + per_wg - 1) / per_wg;
+  const long slots_wanted = (long)kNumCU * (p.NW == 4 ? 2 : 1);
+  long want = (slots_wanted + units * n_mt - 1) / (units * n_mt);
   const long by_len = n_tiles / 2 > 0 ? n_tiles / 2 : 1;  // at least 2 tiles per split
   if (want > by_len) want = by_len;
   finish_plan(p, B, T_cap, H, Hkv, max_ctx, (int)want);
