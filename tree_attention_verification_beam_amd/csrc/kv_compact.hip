@@ -5,8 +5,10 @@
 // appended to the context and the next step starts after them.  The tree's K/V
 // sit at slots ctx + node; the accepted path's entries move to ctx + 1.., the
 // root staying at ctx.  A destination can be another entry's source
-// (path [0, 2, 3]: slot ctx+2 is both), so a workgroup first gathers all of
-// one head's moved rows into LDS, then scatters them.
+// (path [0, 2, 3]: slot ctx+2 is both), so a workgroup first gathers all the
+// moved rows of its heads into LDS, then scatters them.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace spec {
@@ -15,23 +17,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kArrive = 1 << 24;  // arrival count lives above the context length
 
-// One workgroup per (sequence, KV head, K or V).  Every workgroup of a sequence
+// One workgroup per (sequence, K or V, group of HPG KV heads), sized on the
+// host so that the longest possible path of a group fits its LDS buffer.  Few
+// workgroups per sequence keep the arrival count below (one same-address
+// atomic per workgroup) cheap.  Every workgroup of a sequence
 // first adds kArrive to ctx_len[b] atomically: the low 24 bits of the returned
 // value are the context length before the commit, whatever the arrival order,
 // and the workgroup that arrives last writes the new length (all others have
 // read the old one by then).
 __global__ __launch_bounds__(kThreads) void k_kv_compact(
-    int elem_bytes, int Hkv, int D, int cache_cap, int T_cap, unsigned char* __restrict__ kc,
-    unsigned char* __restrict__ vc, int32_t* __restrict__ ctx_len,
+    int elem_bytes, int Hkv, int HPG, int G, int D, int cache_cap, int T_cap,
+    unsigned char* __restrict__ kc, unsigned char* __restrict__ vc, int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path,
     int32_t* __restrict__ status) {
-  extern __shared__ __align__(16) unsigned char buf[];  // [T_cap - 1][row bytes]
+  static_assert(kThreads >= SPEC_MAX_TREE, "one path entry per thread");
+  extern __shared__ uint4 buf[];  // [HPG * longest path * row words]
   __shared__ int s_src[SPEC_MAX_TREE];
   __shared__ int s_ok, s_ctx, s_last;
-  static_assert(kThreads >= SPEC_MAX_TREE, "one path entry per thread");
   const int b = blockIdx.x;
-  const int g = blockIdx.y >> 1;
-  const int which = blockIdx.y & 1;
+  const int which = blockIdx.y / G;
+  const int g = blockIdx.y - which * G;
   const int tid = threadIdx.x;
   const int n = acc_len[b];
   const int32_t* path = acc_path + (size_t)b * T_cap;
@@ -42,7 +47,7 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
     const int old = atomicAdd(ctx_len + b, kArrive);
     const int ctx = old & (kArrive - 1);
     s_ctx = ctx;
-    s_last = (old >> 24) == 2 * Hkv - 1;
+    s_last = (old >> 24) == 2 * G - 1;
     s_ok = (n >= 0 && n < T_cap && ctx + n + 1 <= cache_cap) ? 1 : 0;
   }
   if (tid < T_cap) s_src[tid] = my_src;
@@ -56,20 +61,45 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
   __syncthreads();
   if (s_ok) {
     const int row16 = D * elem_bytes / 16;  // 16-byte words per row
-    unsigned char* base = (which ? vc : kc) + ((size_t)b * Hkv + g) * cache_cap * D * elem_bytes;
-    for (int e = tid; e < n * row16; e += kThreads) {
-      const int i = 1 + e / row16, w = e - (e / row16) * row16;
+    const int per_head = n * row16;
+    const int h0 = g * HPG;
+    const int nh = min(HPG, Hkv - h0);
+    const int total = nh * per_head;  // fits the LDS buffer (sized on the host)
+    const size_t head_bytes = (size_t)cache_cap * D * elem_bytes;
+    unsigned char* base = (which ? vc : kc) + ((size_t)b * Hkv + h0) * head_bytes;
+    // kBatch loads in flight per thread: every load is issued (a unit past the
+    // end reads the group's first word as a stand-in) and only the LDS store
+    // is predicated, so the loads do not wait on one another
+    constexpr int kBatch = 4;
+    auto unit = [&](int e, bool& keep) -> uint4 {
+      const bool in = e < total;
+      const int ec = in ? e : 0;
+      const int h = ec / per_head, rem = ec - (ec / per_head) * per_head;
+      const int i = 1 + rem / row16, w = rem - (rem / row16) * row16;
       const int src = s_src[i];
-      if (src == i) continue;
-      reinterpret_cast<uint4*>(buf)[(size_t)(i - 1) * row16 + w] =
-          reinterpret_cast<const uint4*>(base + (size_t)(ctx + src) * D * elem_bytes)[w];
+      keep = in && src != i;
+      const size_t off = in ? h * head_bytes + (size_t)(ctx + src) * D * elem_bytes + w * 16 : 0;
+      return *reinterpret_cast<const uint4*>(base + off);
+    };
+    for (int e0 = tid; e0 < total; e0 += kBatch * kThreads) {
+      bool k0, k1, k2, k3;
+      const uint4 t0 = unit(e0, k0);
+      const uint4 t1 = unit(e0 + kThreads, k1);
+      const uint4 t2 = unit(e0 + 2 * kThreads, k2);
+      const uint4 t3 = unit(e0 + 3 * kThreads, k3);
+      __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its stores
+      if (k0) buf[e0] = t0;
+      if (k1) buf[e0 + kThreads] = t1;
+      if (k2) buf[e0 + 2 * kThreads] = t2;
+      if (k3) buf[e0 + 3 * kThreads] = t3;
     }
-    __syncthreads();
-    for (int e = tid; e < n * row16; e += kThreads) {
-      const int i = 1 + e / row16, w = e - (e / row16) * row16;
-      if (s_src[i] == i) continue;
-      reinterpret_cast<uint4*>(base + (size_t)(ctx + i) * D * elem_bytes)[w] =
-          reinterpret_cast<const uint4*>(buf)[(size_t)(i - 1) * row16 + w];
+    __syncthreads();  // every source read before any destination is written
+    for (int e = tid; e < total; e += kThreads) {
+      const int h = e / per_head, rem = e - (e / per_head) * per_head;
+      const int i = 1 + rem / row16, w = rem - (rem / row16) * row16;
+      if (s_src[i] != i)
+        reinterpret_cast<uint4*>(base + h * head_bytes + (size_t)(ctx + i) * D * elem_bytes)[w] =
+            buf[e];
     }
   }
   if (tid == 0 && s_last) {
@@ -106,10 +136,21 @@ extern "C" int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int
   if (B == 0) return SPEC_OK;
   if (!k_cache || !v_cache || !ctx_len || !acc_len || !acc_path) return SPEC_ERR_INVALID;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return SPEC_ERR_INVALID;
-  const size_t lds = (size_t)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb;
-  if (lds > 64 * 1024) return SPEC_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(k_kv_compact, dim3(B, 2 * Hkv), dim3(kThreads), lds, as_stream(stream), eb,
-                     Hkv, D, cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
+  // heads per workgroup: the longest path a group can commit fits 64 KiB of LDS
+  constexpr long kBufWords = 64 * 1024 / 16;
+  const long per_head_max = (long)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb / 16;
+  if (per_head_max > kBufWords) return SPEC_ERR_UNSUPPORTED;
+  int HPG = (int)(kBufWords / per_head_max);
+  if (HPG > Hkv) HPG = Hkv;
+  // small batches get more groups (more workgroups in flight), large ones
+  // fewer (fewer same-address arrivals per sequence): about 64 groups overall
+  const int g_min = (Hkv + HPG - 1) / HPG;  // fewest groups the buffer allows
+  const int g_want = std::min(Hkv, (64 + B - 1) / B);
+  if (g_want > g_min) HPG = (Hkv + g_want - 1) / g_want;
+  const int G = (Hkv + HPG - 1) / HPG;
+  const size_t lds = (size_t)HPG * per_head_max * 16;
+  hipLaunchKernelGGL(k_kv_compact, dim3(B, 2 * G), dim3(kThreads), lds, as_stream(stream), eb,
+                     Hkv, HPG, G, D, cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
                      static_cast<unsigned char*>(v_cache), ctx_len, acc_len, acc_path, status);
   return launch_status();
 }

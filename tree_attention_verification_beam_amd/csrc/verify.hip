@@ -267,6 +267,7 @@ struct SelArgs {
 
 // Shared state of one sequence inside a select workgroup.
 struct SelShared {
+  int row[SPEC_MAX_TREE];  // draft row of every node (rejection modes)
   int par[SPEC_MAX_TREE];
   int tok[SPEC_MAX_TREE];
   int dep[SPEC_MAX_TREE];
@@ -726,7 +727,21 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
 
   const size_t nb = (size_t)b * T_cap;
   __shared__ int s_bad;
+  static_assert(kSelThreads >= SPEC_MAX_TREE, "one tree row per thread");
+  // One round trip for the tree and, in greedy mode, for the chunk partials of
+  // every target row the tree can have (rows past n_nodes are never used).
   const int T_in = A.n_nodes[b];
+  int my_par = -1, my_tok = 0, my_dep = 0, my_row = 0;
+  if (tid < T_cap) {
+    my_par = tid == 0 ? -1 : A.parent[nb + tid];
+    my_tok = A.token[nb + tid];
+    my_dep = tid == 0 ? 0 : A.depth[nb + tid];
+    if (MODE != SPEC_GREEDY) my_row = A.dft_row[nb + tid];
+  }
+  const bool staged = MODE == SPEC_GREEDY && T_cap * A.n_chunks <= kMergeEntries;
+  if (staged)
+    for (int e = tid; e < T_cap * A.n_chunks; e += kSelThreads)
+      sh.ent[e] = A.part[nb * A.n_chunks + e];
   int T = T_in < 1 ? 1 : (T_in > T_cap ? T_cap : T_in);
 
   // ---------------------------------------------------------------- tree + row stats
@@ -741,10 +756,11 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     s_bad = (T_in < 1 || T_in > T_cap) ? SPEC_DEV_BAD_TREE : 0;
   }
   __syncthreads();
-  for (int t = tid; t < T; t += kSelThreads) {
-    sh.par[t] = t == 0 ? -1 : A.parent[nb + t];
-    sh.tok[t] = A.token[nb + t];
-    sh.dep[t] = t == 0 ? 0 : A.depth[nb + t];
+  if (tid < T) {
+    sh.par[tid] = my_par;
+    sh.tok[tid] = my_tok;
+    sh.dep[tid] = my_dep;
+    sh.row[tid] = my_row;
   }
   __syncthreads();
   // validate the tree against the vocabulary and the draft rows; a bad
@@ -763,7 +779,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   if (MODE != SPEC_GREEDY) {
     for (int t = tid; t < T; t += kSelThreads) {
       if (sh.nch[t] == 0) continue;
-      const int r = A.dft_row[nb + t];
+      const int r = sh.row[t];
       if (r < 0 || r >= A.Rr) atomicOr(&s_bad, SPEC_DEV_BAD_ROW);
     }
     __syncthreads();
@@ -774,6 +790,14 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     T = 1;
     for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) sh.nch[t] = 0;
     __syncthreads();
+  }
+  // The logits of every node's own token under its parent, issued now so
+  // they arrive while the row statistics are merged.
+  double lp_own = 0.0, lq_own = 0.0;
+  if (tid + 1 < T) {
+    const int t = tid + 1, sp = sh.par[t], x = sh.tok[t];
+    lp_own = A.tgt[(nb + sp) * V + x];
+    if (MODE != SPEC_GREEDY) lq_own = A.dft[((size_t)b * A.Rr + sh.row[sp]) * V + x];
   }
   // Row statistics from the vocabulary pass's chunk partials, with all threads:
   // the partials of a batch of rows are staged in LDS, then per row the
@@ -789,7 +813,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     for (int t = tid; t < T; t += kSelThreads) {
       if (sh.nch[t] == 0) continue;
       const int j = atomicAdd(&sh.n_jobs, 1);
-      sh.job_unit[j] = (int)((size_t)A.B * T_cap + (size_t)b * A.Rr + A.dft_row[nb + t]);
+      sh.job_unit[j] = (int)((size_t)A.B * T_cap + (size_t)b * A.Rr + sh.row[t]);
       sh.job_node[j] = -1 - t;
     }
     __syncthreads();
@@ -799,11 +823,13 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     const int per_batch = min(kMergeEntries / nc, 2 * SPEC_MAX_TREE);
     for (int j0 = 0; j0 < n_jobs; j0 += per_batch) {
       const int nj = min(per_batch, n_jobs - j0);
-      for (int e = tid; e < nj * nc; e += kSelThreads) {
-        const int j = j0 + e / nc, cc = e - (e / nc) * nc;
-        sh.ent[e] = A.part[(size_t)sh.job_unit[j] * nc + cc];
+      if (!staged) {  // staged: the target rows' partials are in LDS already
+        for (int e = tid; e < nj * nc; e += kSelThreads) {
+          const int j = j0 + e / nc, cc = e - (e / nc) * nc;
+          sh.ent[e] = A.part[(size_t)sh.job_unit[j] * nc + cc];
+        }
+        __syncthreads();
       }
-      __syncthreads();
       for (int k = tid; k < nj; k += kSelThreads) {
         float m = -INFINITY;
         int arg = 0;
@@ -841,15 +867,10 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     }
   }
   // p and q of every node's own token under its parent (fp64 exp, merged sums)
-  for (int t = tid + 1; t < T; t += kSelThreads) {
-    const int s = sh.par[t], x = sh.tok[t];
-    const double lp = A.tgt[(nb + s) * V + x];
-    sh.pt[t] = exp(lp - (double)sh.m_p[s]) / sh.S_p[s];
-    if (MODE != SPEC_GREEDY) {
-      const int r = A.dft_row[nb + s];
-      const double lq = A.dft[((size_t)b * A.Rr + r) * V + x];
-      sh.qt[t] = exp(lq - (double)sh.m_q[s]) / sh.S_q[s];
-    }
+  if (tid + 1 < T) {
+    const int t = tid + 1, sp = sh.par[t];
+    sh.pt[t] = exp(lp_own - (double)sh.m_p[sp]) / sh.S_p[sp];
+    if (MODE != SPEC_GREEDY) sh.qt[t] = exp(lq_own - (double)sh.m_q[sp]) / sh.S_q[sp];
   }
   __syncthreads();
 
@@ -895,7 +916,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
       rp.lp = A.tgt + (nb + stop) * V;
       rp.mp = sh.m_p[stop];
       if (sh.nch[stop] > 0) {
-        const int r = A.dft_row[nb + stop];
+        const int r = sh.row[stop];
         rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
         rp.mq = sh.m_q[stop];
         if (A.cache) {
@@ -918,7 +939,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
       rp.lp = A.tgt + (nb + s) * V;
       rp.mp = sh.m_p[s];
       if (sh.nch[s] > 0) {
-        const int r = A.dft_row[nb + s];
+        const int r = sh.row[s];
         rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
         rp.mq = sh.m_q[s];
       }

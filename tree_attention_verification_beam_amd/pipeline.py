@@ -123,6 +123,24 @@ class Step:
             self.p_reset = P("spec_copy_probe", self.ctx0, self.ctx_len, self.ctx_bytes,
                              stream=stream)
 
+    def prepare_fresh_contexts(self, n, stream=None):
+        """n copies of the initial context lengths, each with its own prepared
+        attention and commit calls.  A timing loop that uses copy k for the
+        k-th step of this input set starts every step from the same context
+        without a restore in the timed region (the commit advances the copy
+        it was given)."""
+        P = sv.prepare
+        self.fresh_ctx = [self.ctx0.clone() for _ in range(n)]
+        self.p_attention_fresh = [
+            P("spec_tree_attention", self.dt, self.B, self.T_cap, self.H, self.Hkv, self.D,
+              self.cap, self.max_ctx, self.q, self.k, self.v, c, self.n_nodes, self.anc, 0.0,
+              self.out, self.attn_ws, self.attn_ws_bytes, self.status, stream=stream)
+            for c in self.fresh_ctx]
+        self.p_compact_fresh = [
+            P("spec_kv_compact", self.dt, self.B, self.Hkv, self.D, self.cap, self.T_cap, self.k,
+              self.v, c, self.acc_len, self.acc_path, self.status, stream=stream)
+            for c in self.fresh_ctx]
+
     # ------------------------------------------------------------------ calls
     def build_tree(self, stream=None):
         sv.spec_build_tree(self.kind, self.B, self.W, self.L, self.T_cap, self.cand_token,
