@@ -421,10 +421,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         lvis[i] = h ? sw : v;
       }
     }
+    // Scores of all this wave's keys of the tile first, then one online-softmax
+    // step over them (one maximum check and rescale per tile), then P V: the
+    // MFMA work of the tile comes in two blocks with the VALU work between.
+    f32x4 sacc[PV_STEPS][QT][2];
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
       const int ck0 = wkey0 + 32 * j;  // first key of the chunk inside the tile
-      f32x4 sacc[QT][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bf16x8 kf[KSTEPS];
@@ -440,72 +443,81 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           f32x4 cc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < KSTEPS; ++s) cc = mfma16x16x32(kf[s], qf[i][s], cc);
-          sacc[i][st] = cc;
+          sacc[j][i][st] = cc;
         }
       }
+    }
 
-      // keys past the range or outside the node's ancestor set score -inf
-      if (need_mask) {
+    // keys past the range or outside the node's ancestor set score -inf
+    if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < QT; ++i) {
+      for (int j = 0; j < PV_STEPS; ++j)
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
+        for (int i = 0; i < QT; ++i)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int c = 32 * j + 4 * st + e;  // compile-time bit position
               const uint32_t word = c < 32 ? (uint32_t)lvis[i] : (uint32_t)(lvis[i] >> 32);
               const bool vis = (word >> (c & 31)) & 1u;
-              sacc[i][st][e] = vis ? sacc[i][st][e] : -INFINITY;
+              sacc[j][i][st][e] = vis ? sacc[j][i][st][e] : -INFINITY;
             }
-          }
-        }
-      }
+    }
 
-      // online softmax in exp2 form; lane owns query l16, keys ck0 + 8 lg + 4 (st ^ h) + e
-      bf16x8 pf[QT];
+    // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
+    // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e
+    bf16x8 pf[PV_STEPS][QT];
 #pragma unroll
-      for (int i = 0; i < QT; ++i) {
-        float lmax = fmaxf(fmaxf(fmaxf(sacc[i][0][0], sacc[i][0][1]),
-                                 fmaxf(sacc[i][0][2], sacc[i][0][3])),
-                           fmaxf(fmaxf(sacc[i][1][0], sacc[i][1][1]),
-                                 fmaxf(sacc[i][1][2], sacc[i][1][3])));
-        lmax *= c;
-        // the row maximum moves only when some lane outgrew it by 2^kRescale;
-        // then the 4 lane groups holding the row agree on the new maximum
-        if (__builtin_amdgcn_ballot_w64(lmax > m_run[i] + kRescale) != 0ull) {
-          float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
-          tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
-          const float m_new = fmaxf(m_run[i], tmax);
-          const float alpha =
-              (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
-          l_run[i] *= alpha;
+    for (int i = 0; i < QT; ++i) {
+      float lmax = -INFINITY;
 #pragma unroll
-          for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
-          m_run[i] = m_new;
-        }
-        const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
-        float psum = 0.0f;
+      for (int j = 0; j < PV_STEPS; ++j)
+        lmax = fmaxf(lmax, fmaxf(fmaxf(fmaxf(sacc[j][i][0][0], sacc[j][i][0][1]),
+                                       fmaxf(sacc[j][i][0][2], sacc[j][i][0][3])),
+                                 fmaxf(fmaxf(sacc[j][i][1][0], sacc[j][i][1][1]),
+                                       fmaxf(sacc[j][i][1][2], sacc[j][i][1][3]))));
+      lmax *= c;
+      // the row maximum moves only when some lane outgrew it by 2^kRescale;
+      // then the 4 lane groups holding the row agree on the new maximum
+      if (__builtin_amdgcn_ballot_w64(lmax > m_run[i] + kRescale) != 0ull) {
+        float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        const float m_new = fmaxf(m_run[i], tmax);
+        const float alpha =
+            (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+        l_run[i] *= alpha;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
+        m_run[i] = m_new;
+      }
+      const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
+      float psum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < PV_STEPS; ++j)
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i][st][e], c, nmu));
-            pf[i][4 * st + e] = (bf16_t)pv;
+            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
+            pf[j][i][4 * st + e] = (bf16_t)pv;
             psum += pv;
           }
-        }
-        l_run[i] += psum;
-      }
+      l_run[i] += psum;
+    }
 
-      // O^T += V^T P^T over the chunk's 32 keys: this lane's 8 P values are
-      // the keys ck0 + 8 lg .. + 7 in V^T column order, one 16-byte read
+    // O^T += V^T P^T over the tile: in chunk j this lane's 8 P values are the
+    // keys wkey0 + 32 j + 8 lg .. + 7 in V^T column order, one 16-byte read
+#pragma unroll
+    for (int j = 0; j < PV_STEPS; ++j) {
+      const int ck0 = wkey0 + 32 * j;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
         const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
         const int sw = Lds<D>::swz(16 * d);  // the same for rows 16d .. 16d+15
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + ((ck0 + 8 * lg) ^ sw));
 #pragma unroll
-        for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[i], acc[i][d]);
+        for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[j][i], acc[i][d]);
       }
     }
   };
