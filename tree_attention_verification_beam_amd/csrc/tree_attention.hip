@@ -117,14 +117,18 @@ size_t partial_bytes(const AttnPlan& p, int B, int T_cap, int H, int Hkv, int D)
 // h(q) = (q >> 1) & 1.  The lane group q of the output then holds 8 of the
 // chunk's keys, 8 q .. 8 q + 7, so its P values form one 16-byte operand read
 // of a transposed V row, provided V^T stores key k at column vcol(k) below,
-// which swaps the two 4-key halves of every 8-key block with h = 1.  The
-// permutation h, the row pitches and the row swizzle swz keep the K operand
-// reads (16 lanes x 16 bytes per phase), the V^T stores and the V^T operand
-// reads of a wave on distinct banks of a 64-bank LDS.
+// which swaps the two 4-key halves of every 8-key block with h = 1.  The row
+// pitches and the V^T row swizzle swz keep the K operand reads, the V^T
+// stores and the V^T operand reads of a wave free of bank conflicts.  The
+// pitches come from a conflict rule measured on gfx950 with
+// SQ_LDS_BANK_CONFLICT: 64 banks of 4 bytes; a 16-byte read is served in four
+// passes of 16 lanes, and a bank group hit from different lane positions in
+// different passes costs extra passes.  Rows of D + 16 and 64 + 16 elements
+// read these patterns conflict-free; D + 8 and 64 + 8 read them 2-way.
 template <int D>
 struct Lds {
-  static constexpr int kPitchK = D + 8;         // bf16 elements per K row
-  static constexpr int kPitchV = kKeyTile + 8;  // bf16 elements per transposed V row
+  static constexpr int kPitchK = D + 16;         // bf16 elements per K row
+  static constexpr int kPitchV = kKeyTile + 16;  // bf16 elements per transposed V row
   static __device__ constexpr int swz(int row) { return ((row >> 4) & 7) * 8; }
   static __device__ constexpr int vcol(int key, int row) {
     return key ^ (((key >> 4) & 1) * 4) ^ swz(row);
