@@ -185,6 +185,30 @@ def verify(mode, tgt: np.ndarray, dft, dft_row, n_nodes, parent, token, depth, u
     return out
 
 
+def verify_greedy_walk(tgt: np.ndarray, n_nodes, parent, token, depth):
+    """Greedy verification by a depth-by-depth walk over the surviving nodes; see
+    orc_verify_greedy_walk in oracle.c.  Only tested nodes carry decision/p_tok."""
+    tgt = np.ascontiguousarray(tgt, dtype=np.float32)
+    B, T_cap, V = tgt.shape
+    out = dict(
+        acc_len=np.zeros(B, np.int32),
+        acc_path=np.zeros((B, T_cap), np.int32),
+        next_token=np.zeros(B, np.int32),
+        p_tok=np.zeros((B, T_cap), np.float64),
+        q_tok=np.zeros((B, T_cap), np.float64),
+        decision=np.zeros((B, T_cap), np.int8),
+        near_tie=np.zeros(B, np.int32),
+        rows_read=np.zeros(B, np.int32),
+    )
+    f = lib().orc_verify_greedy_walk
+    f.restype = ctypes.c_int
+    rc = f(B, T_cap, V, _p(tgt), _p(_i32(n_nodes)), _p(_i32(parent)), _p(_i32(token)),
+           _p(_i32(depth)), _p(out["acc_len"]), _p(out["acc_path"]), _p(out["next_token"]),
+           _p(out["p_tok"]), _p(out["decision"]), _p(out["rows_read"]))
+    _check(rc, "verify_greedy_walk")
+    return out
+
+
 def residual_chain(p: np.ndarray, q: np.ndarray, K: int, literal: bool = False):
     """Residual distributions after 0..K rejections: (dist [K+1][V], mass [K+1], filled)."""
     p = np.ascontiguousarray(p, dtype=np.float64)

@@ -563,6 +563,90 @@ int orc_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, const
 }
 
 /*
+ * Greedy verification by walking the tree from the root ([ReDrafter] section
+ * "The Full Speculative Decoding Loop", Step 5, token matches): the same
+ * acceptance as orc_verify in ORC_GREEDY, found by visiting only the rows that
+ * the decision needs.  The nodes whose whole path is accepted are explored
+ * depth by depth: the frontier starts as {root}; every frontier node's target
+ * row gives its greedy token (argmax, lowest index on ties); its children are
+ * tested against it, and the accepted ones form the next frontier.  The stop
+ * node is the lowest-index node of the deepest non-empty frontier (the deepest
+ * survivor, lowest index on ties) and the next token is its greedy token.
+ *
+ * Outputs as orc_verify, except that only tested nodes (children of frontier
+ * nodes) get decision (1 / 0) and p_tok; all other entries are -1 and 0.
+ * rows_read[b] counts the target rows read: one per frontier node.
+ */
+int orc_verify_greedy_walk(int B, int T_cap, int V, const float *tgt, const int32_t *n_nodes,
+                           const int32_t *parent, const int32_t *token, const int32_t *depth,
+                           int32_t *acc_len, int32_t *acc_path, int32_t *next_token,
+                           double *p_tok, int8_t *decision, int32_t *rows_read)
+{
+    if (B < 0 || T_cap < 1 || V < 1) return ORC_ERR;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    int *front = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *next = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *greedy = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    if (!p || !front || !next || !greedy) {
+        free(p); free(front); free(next); free(greedy);
+        return ORC_ERR;
+    }
+    int rc = ORC_OK;
+    for (int b = 0; b < B && rc == ORC_OK; ++b) {
+        const int T = n_nodes[b];
+        const int32_t *par = parent + (size_t)b * T_cap;
+        const int32_t *tok = token + (size_t)b * T_cap;
+        const int32_t *dep = depth + (size_t)b * T_cap;
+        int32_t *path = acc_path + (size_t)b * T_cap;
+        int8_t *dec = decision + (size_t)b * T_cap;
+        double *pt = p_tok + (size_t)b * T_cap;
+        if (T < 1 || T > T_cap) { rc = ORC_ERR; break; }
+        for (int t = 1; t < T; ++t)
+            if (par[t] < 0 || par[t] >= t || tok[t] < 0 || tok[t] >= V) { rc = ORC_ERR; break; }
+        if (rc != ORC_OK) break;
+        for (int t = 0; t < T_cap; ++t) {
+            path[t] = -1;
+            dec[t] = -1;
+            pt[t] = 0.0;
+        }
+        int n_front = 1, stop = 0, reads = 0;
+        front[0] = 0;
+        while (n_front > 0) {
+            /* the frontier is in increasing node order: its first node is the
+             * lowest-index survivor of this depth */
+            stop = front[0];
+            int n_next = 0;
+            for (int i = 0; i < n_front; ++i) {
+                const int f = front[i];
+                const float *row = tgt + ((size_t)b * T_cap + f) * V;
+                greedy[f] = argmax_row(V, row);
+                softmax_row(V, row, p);
+                ++reads;
+                for (int c = f + 1; c < T; ++c) {
+                    if (par[c] != f) continue;
+                    dec[c] = (int8_t)(tok[c] == greedy[f]);
+                    pt[c] = p[tok[c]];
+                    if (dec[c]) next[n_next++] = c;
+                }
+            }
+            /* children of different frontier nodes interleave in index order */
+            for (int i = 1; i < n_next; ++i)
+                for (int j = i; j > 0 && next[j - 1] > next[j]; --j) {
+                    const int x = next[j]; next[j] = next[j - 1]; next[j - 1] = x;
+                }
+            memcpy(front, next, sizeof(int) * (size_t)n_next);
+            n_front = n_next;
+        }
+        acc_len[b] = dep[stop];
+        for (int cur = stop; cur >= 0; cur = par[cur]) path[dep[cur]] = cur;
+        next_token[b] = greedy[stop];
+        rows_read[b] = reads;
+    }
+    free(p); free(front); free(next); free(greedy);
+    return rc;
+}
+
+/*
  * Residual chain of one (p, q) pair, for pins of the closed form.
  * literal = 0: closed form, c_0 = 0, Z_0 = 1, c_{k+1} = c_k + Z_k,
  *   Z_{k+1} = sum max(0, p - c_{k+1} q); dist_k = max(0, p - c_k q) / Z_k.
