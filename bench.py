@@ -41,7 +41,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=1)
-    ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive")
+    ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive | greedy_walk")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
@@ -93,18 +93,23 @@ def attention_bytes(inp, n_nodes):
     return total
 
 
-def verify_bytes(inp, n_nodes, parent, dft_row, mode):
-    """Algorithmic HBM bytes of one spec_verify launch (one pass over every needed row).
+def verify_bytes(inp, n_nodes, parent, dft_row, mode, decision=None):
+    """Algorithmic HBM bytes of one spec_verify launch.
 
-    Every target row of the tree (any node can be the stop node) and, in the
-    rejection modes, every draft row of a node with children.
+    One pass over every needed row: every target row of the tree (any node can
+    be the stop node) and, in the rejection modes, every draft row of a node
+    with children.  The greedy walk reads one target row per node whose path is
+    accepted: the root and every accepted tested node (decision == 1).
     """
     V = inp["V"]
     total = 0
     for b in range(inp["B"]):
+        if mode == "greedy_walk":
+            total += (1 + int((decision[b] == 1).sum())) * V * 4
+            continue
         T = int(n_nodes[b])
         total += T * V * 4
-        if mode != "greedy":
+        if mode not in ("greedy", "greedy_walk"):
             has_child = set(int(p) for p in parent[b, 1:T])
             rows = {int(dft_row[b, t]) for t in has_child}
             total += len(rows) * V * 4
@@ -226,7 +231,8 @@ def main():
         nn = st.n_nodes.cpu().numpy()
         a_bytes.append(attention_bytes(inp, nn))
         v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
-                                    inp["dft_row"] if inp["dft_row"] is not None else None, mode))
+                                    inp["dft_row"] if inp["dft_row"] is not None else None, mode,
+                                    st.decision.cpu().numpy()))
     a_avg = float(np.mean([a_bytes[i % n_sets] for i in range(args.steps)]))
     v_avg = float(np.mean(v_bytes))
     achieved = a_avg / attn_avg_s / 1e9
@@ -287,9 +293,13 @@ def cpu_baseline(inp, mode, budget_s):
         oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
                               tr["anc"])
         g = mode == "greedy"
-        res = oracle.verify(mode, inp["tgt"], None if g else inp["dft"],
-                            None if g else inp["dft_row"], tr["n_nodes"], tr["parent"],
-                            tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
+        if mode == "greedy_walk":
+            res = oracle.verify_greedy_walk(inp["tgt"], tr["n_nodes"], tr["parent"],
+                                            tr["token"], tr["depth"])
+        else:
+            res = oracle.verify(mode, inp["tgt"], None if g else inp["dft"],
+                                None if g else inp["dft_row"], tr["n_nodes"], tr["parent"],
+                                tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
         k, v = inp["k"].copy(), inp["v"].copy()
         oracle.kv_compact(k, v, inp["ctx_len"], res["acc_len"], res["acc_path"])
         t_total += time.perf_counter() - t0

@@ -76,7 +76,8 @@ typedef enum { SPEC_TREE_BEAMS = 0, SPEC_TREE_EXPLICIT = 1 } spec_tree_kind;
 typedef enum {
     SPEC_GREEDY = 0,
     SPEC_REJECT_PATH = 1,
-    SPEC_REJECT_RECURSIVE = 2
+    SPEC_REJECT_RECURSIVE = 2,
+    SPEC_GREEDY_WALK = 3
 } spec_verify_mode;
 
 /* Library version as 10000*major + 100*minor + patch (host only). */
@@ -170,6 +171,15 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  *                         p' <- norm(max(0, p' - q_s)).  An acceptance moves to
  *                         that child.  With no child left, the next token is
  *                         drawn from p' with u_final.
+ *   SPEC_GREEDY_WALK      the acceptance, stop node and next token of
+ *                         SPEC_GREEDY, found by reading only the target rows
+ *                         of nodes whose whole path is accepted: from the root,
+ *                         depth by depth, each such node's row is scanned and
+ *                         its children are tested.  Only tested nodes (children
+ *                         of such nodes) get decision and p_tok; the others get
+ *                         -1 and 0.  Its workspace must be zero-filled before
+ *                         its first call; every call leaves it ready for the
+ *                         next (its counters back at zero).
  * Draws are inverse-CDF in ascending vocabulary order: the smallest v whose
  * running sum exceeds u_final * total.
  *
@@ -186,7 +196,8 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * fell within 1e-9 of a running-sum boundary).
  * A bad token or missing draft row raises a SPEC_DEV_* bit and the sequence
  * accepts nothing (acc_len 0, next_token = argmax p_0).
- * ws: spec_verify_workspace_size() bytes (no initial contents needed).  Calls
+ * ws: spec_verify_workspace_size() bytes (no initial contents needed, except in
+ * SPEC_GREEDY_WALK: zero-filled before the first call, see above).  Calls
  * that overlap in time must not share a workspace.
  */
 size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R);

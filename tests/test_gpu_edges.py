@@ -8,7 +8,10 @@
 - a context that overflows the launch bound: that sequence gets zero rows and
   the device status bit, the others stay exact;
 - B = 0 calls (host-only, in test_abi.py);
-- one attention call launched forty times, each checked (intermittent errors).
+- one attention call launched forty times, each checked (intermittent errors);
+- the greedy walk on explicit trees whose siblings share tokens (several
+  survivors per depth), on a vocabulary that is not a multiple of 4 (scalar
+  loads) and on a tree that fails validation.
 Bar as in test_gpu_parity.py.
 """
 import numpy as np
@@ -23,7 +26,7 @@ from test_gpu_parity import (assert_tree_equal, assert_verify_equal, attn_bar, l
 
 pytestmark = pytest.mark.gpu
 
-MODES = ("greedy", "reject_path", "reject_recursive")
+MODES = ("greedy", "reject_path", "reject_recursive", "greedy_walk")
 
 
 def run_all_modes(gpu, inp, what, planted=True):
@@ -60,11 +63,12 @@ def run_all_modes(gpu, inp, what, planted=True):
                 par = int(tr["parent"][b, t])
                 tgt[b, par, tr["token"][b, t]] = tgt[b, par].max() + 20.0
         inp2 = dict(inp, tgt=tgt)
-        step = pipeline.Step(inp2, "greedy", with_kv=False)
-        res = step.run()
-        ref = oracle_verify(inp2, tr, "greedy")
-        assert_verify_equal(res, ref, f"{what} greedy planted")
-        assert ref["acc_len"].min() >= 1
+        for mode in ("greedy", "greedy_walk"):
+            step = pipeline.Step(inp2, mode, with_kv=False)
+            res = step.run()
+            ref = oracle_verify(inp2, tr, mode)
+            assert_verify_equal(res, ref, f"{what} {mode} planted")
+            assert ref["acc_len"].min() >= 1
 
 
 def test_largest_tree_ragged_context(gpu):
@@ -150,3 +154,84 @@ def test_attention_repeated_launches_match(gpu):
         torch.cuda.synchronize()
         assert int(step.status.item()) == 0
         attn_bar(step.out.float().cpu().numpy(), ref, f"launch {rep}")
+
+
+def test_greedy_walk_duplicate_siblings_and_odd_vocab(gpu):
+    """Explicit trees whose siblings repeat a token: several nodes of one depth
+    survive, and the walk scans all their rows in node order.  V = 3001 takes the
+    scalar-load scan; V = 3000 the 16-byte one."""
+    parents = [0, 0, 0, 1, 1, 2, 3, 3, 4, 6, 6, 7, 9, 9, 10, 0, 15, 15]
+    for V in (3000, 3001):
+        inp = synth.make_custom_inputs(9010 + V, B=6, H=4, Hkv=4, D=64, V=V, dtype="bf16",
+                                       ctx_lens=[8] * 6, tree="explicit", parents=parents)
+        rng = np.random.default_rng(V)
+        inp["cand_token"] = rng.integers(0, 3, size=inp["cand_token"].shape).astype(np.int32)
+        tr = oracle_tree(inp)
+        tgt = inp["tgt"].copy()
+        for b in range(inp["B"]):
+            for t in range(int(tr["n_nodes"][b])):
+                if rng.random() < 0.7:
+                    tgt[b, t, rng.integers(0, 3)] = tgt[b, t].max() + 5.0
+        inp2 = dict(inp, tgt=tgt)
+        log(f"case greedy walk, duplicate siblings, V={V}")
+        ref = oracle_verify(inp2, tr, "greedy_walk")
+        assert (ref["rows_read"] >= 3).any()
+        step = pipeline.Step(inp2, "greedy_walk", with_kv=False)
+        res = step.run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_verify_equal(res, ref, f"walk duplicates V={V}")
+        full = oracle_verify(inp2, tr, "greedy")
+        for key in ("acc_len", "acc_path", "next_token"):
+            assert np.array_equal(res[key], full[key]), key
+
+
+def test_greedy_walk_bad_tree(gpu):
+    """A candidate naming a later parent: the tree build flags the sequence and
+    the walk accepts nothing and takes the root's greedy token."""
+    inp = synth.make_inputs(4, 301, B_override=2, ctx_override=100)
+    inp["cand_parent"] = inp["cand_parent"].copy()
+    inp["cand_parent"][1, 5] = 9
+    log("case greedy walk on a flagged tree")
+    step = pipeline.Step(inp, "greedy_walk")
+    res = step.run()
+    assert res["status"] & 0x1
+    assert res["acc_len"][1] == 0 and res["acc_path"][1, 0] == 0
+    assert np.all(res["acc_path"][1, 1:] == -1) and np.all(res["decision"][1] == -1)
+    assert res["next_token"][1] == int(np.argmax(inp["tgt"][1, 0]))
+    tr = oracle_tree(inp)
+    ref = oracle.verify_greedy_walk(inp["tgt"][:1], tr["n_nodes"][:1], tr["parent"][:1],
+                                    tr["token"][:1], tr["depth"][:1])
+    for key in ("acc_len", "acc_path", "next_token", "decision"):
+        assert np.array_equal(res[key][:1], ref[key]), key
+
+
+def test_greedy_walk_reuses_its_workspace(gpu):
+    """The walk's meeting counters return to zero after every call: two input
+    sets alternate on one workspace (a stale counter would let a meeting read
+    entries of the other set), each call checked against the oracle.  The row
+    slices of a 32k vocabulary go to several workgroups per sequence."""
+    sets = []
+    for seed in (302, 303):
+        inp = synth.make_inputs(1, seed)
+        tr = oracle_tree(inp)
+        inp2 = dict(inp, tgt=plant_greedy_all(inp, tr) if seed == 302 else inp["tgt"])
+        sets.append((inp2, oracle_verify(inp2, tr, "greedy_walk")))
+    assert sets[0][1]["acc_len"][0] >= 2
+    log("case greedy walk, two input sets alternating on one workspace")
+    steps = [pipeline.Step(inp, "greedy_walk", with_kv=False) for inp, _ in sets]
+    steps[1].ver_ws, steps[1].ver_ws_bytes = steps[0].ver_ws, steps[0].ver_ws_bytes
+    for rep in range(6):
+        st, (_, ref) = steps[rep % 2], sets[rep % 2]
+        res = st.run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_verify_equal(res, ref, f"walk call {rep}")
+
+
+def plant_greedy_all(inp, tr):
+    """Make the first beam's whole path the greedy path of every sequence."""
+    tgt = inp["tgt"].copy()
+    for b in range(inp["B"]):
+        for k in range(inp["L"]):
+            par = 0 if k == 0 else tr["beam_node"][b, 0, k - 1]
+            tgt[b, par, inp["beams"][b, 0, k]] = tgt[b, par].max() + 20.0
+    return tgt

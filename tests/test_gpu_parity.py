@@ -28,7 +28,8 @@ REDUCED = {
     3: dict(B_override=2, ctx_override=1000),
     4: dict(B_override=1, ctx_override=3000),
 }
-EXTRA_MODES = {0: ("reject_recursive",), 1: ("reject_recursive",)}
+EXTRA_MODES = {0: ("reject_recursive", "greedy_walk"), 1: ("reject_recursive", "greedy_walk"),
+               2: ("greedy_walk",)}
 
 
 def log(*a):
@@ -45,6 +46,9 @@ def oracle_tree(inp):
 
 def oracle_verify(inp, tr, mode, tgt=None):
     tgt = inp["tgt"] if tgt is None else tgt
+    if mode == "greedy_walk":
+        return oracle.verify_greedy_walk(tgt, tr["n_nodes"], tr["parent"], tr["token"],
+                                         tr["depth"])
     g = mode == "greedy"
     return oracle.verify(mode, tgt, None if g else inp["dft"], None if g else inp["dft_row"],
                          tr["n_nodes"], tr["parent"], tr["token"], tr["depth"], inp["u_node"],
@@ -131,11 +135,12 @@ def test_reduced_workload(gpu, wid, seed):
     if inp["tree"] == "beams":
         tgt = plant_greedy(inp, tr, seed)
         inp2 = dict(inp, tgt=tgt)
-        step = pipeline.Step(inp2, "greedy", with_kv=False)
-        res = step.run()
-        ref = oracle_verify(inp2, tr, "greedy")
-        assert_verify_equal(res, ref, f"wid={wid} greedy planted")
-        assert ref["acc_len"].max() >= 1
+        for mode in ("greedy", "greedy_walk"):
+            step = pipeline.Step(inp2, mode, with_kv=False)
+            res = step.run()
+            ref = oracle_verify(inp2, tr, mode)
+            assert_verify_equal(res, ref, f"wid={wid} {mode} planted")
+            assert ref["acc_len"].max() >= 1
 
 
 # --------------------------------------------------------------------------- full size
@@ -190,6 +195,13 @@ def test_full_size(gpu, full):
         assert torch.equal(step.k[b][:, :ctx[b] + 1], k_before[b][:, :ctx[b] + 1])
     assert np.array_equal(step.ctx_len[:inp["B"]].cpu().numpy(), ctx + res["acc_len"] + 1)
     assert int(step.status.item()) == 0
+    if mode == "greedy":
+        # the walk at full size: the same acceptance from the rows it visits
+        step = pipeline.Step(inp, "greedy_walk", with_kv=False)
+        res = step.run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        assert_verify_equal(res, oracle_verify(inp, tr, "greedy_walk"),
+                            f"full wid={wid} greedy_walk")
 
 
 # --------------------------------------------------------------------------- edge cases

@@ -15,9 +15,9 @@ LIB_PATH = _PKG / "libspecverify.so"
 
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_TREE_BEAMS, SPEC_TREE_EXPLICIT = 0, 1
-SPEC_GREEDY, SPEC_REJECT_PATH, SPEC_REJECT_RECURSIVE = 0, 1, 2
+SPEC_GREEDY, SPEC_REJECT_PATH, SPEC_REJECT_RECURSIVE, SPEC_GREEDY_WALK = 0, 1, 2, 3
 MODES = {"greedy": SPEC_GREEDY, "reject_path": SPEC_REJECT_PATH,
-         "reject_recursive": SPEC_REJECT_RECURSIVE}
+         "reject_recursive": SPEC_REJECT_RECURSIVE, "greedy_walk": SPEC_GREEDY_WALK}
 
 DEV_BITS = {
     0x1: "BAD_PARENT", 0x2: "BAD_TOKEN", 0x4: "BAD_ROW", 0x8: "CTX_RANGE",

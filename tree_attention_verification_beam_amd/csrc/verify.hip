@@ -29,6 +29,15 @@
 #include "common.hpp"
 
 namespace spec {
+
+// greedy walk (verify_walk.hip)
+int launch_verify_walk(int B, int T_cap, int V, const float* tgt, const int32_t* n_nodes,
+                       const int32_t* parent, const int32_t* token, const int32_t* depth,
+                       int32_t* acc_len, int32_t* acc_path, int32_t* next_token, float* p_tok,
+                       float* q_tok, int8_t* decision, int32_t* near_tie, void* ws,
+                       size_t ws_bytes, int32_t* status, hipStream_t s);
+size_t verify_walk_workspace_size(int B);
+
 namespace {
 
 constexpr int kStatThreads = 256;
@@ -1108,6 +1117,7 @@ void launch_stats(const VerifyPlan& pl, bool vec, int B, int T_cap, int V, int R
 using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R) {
+  if (mode == SPEC_GREEDY_WALK && B >= 1) return verify_walk_workspace_size(B);
   if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE || B < 1 || T_cap < 1 || V < 1)
     return 0;
   return make_plan(mode, B, T_cap, V, R).total;
@@ -1120,12 +1130,16 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
                            int32_t* acc_path, int32_t* next_token, float* p_tok, float* q_tok,
                            int8_t* decision, int32_t* near_tie, void* ws, size_t ws_bytes,
                            int32_t* status, void* stream) {
-  if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE) return SPEC_ERR_INVALID;
+  if (mode < SPEC_GREEDY || mode > SPEC_GREEDY_WALK) return SPEC_ERR_INVALID;
   if (B < 0 || T_cap < 1 || V < 1 || R < 0) return SPEC_ERR_INVALID;
   if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
   if (B == 0) return SPEC_OK;
   if (!tgt || !n_nodes || !parent || !token || !depth || !acc_len || !acc_path || !next_token)
     return SPEC_ERR_INVALID;
+  if (mode == SPEC_GREEDY_WALK)
+    return launch_verify_walk(B, T_cap, V, tgt, n_nodes, parent, token, depth, acc_len,
+                              acc_path, next_token, p_tok, q_tok, decision, near_tie, ws,
+                              ws_bytes, status, as_stream(stream));
   if (mode != SPEC_GREEDY) {
     if (!dft || !dft_row || R < 1 || !u_node || !u_final) return SPEC_ERR_INVALID;
   }

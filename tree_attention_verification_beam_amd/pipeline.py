@@ -77,7 +77,7 @@ class Step:
             self.attn_ws_bytes = nb
         # verify
         self.tgt = _dev(inp["tgt"], dev)
-        if self.mode != sv.SPEC_GREEDY:
+        if self.mode not in (sv.SPEC_GREEDY, sv.SPEC_GREEDY_WALK):
             self.dft = _dev(inp["dft"], dev)
             self.dft_row = _dev(inp["dft_row"], dev)
             self.R = int(self.dft.shape[1])
@@ -94,7 +94,8 @@ class Step:
         self.decision = torch.zeros((B, T_cap), dtype=torch.int8, device=dev)
         self.near_tie = torch.zeros(B, **i32)
         nb = sv.spec_verify_workspace_size(self.mode, B, T_cap, V, self.R)
-        self.ver_ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+        # zero-filled once (the greedy walk's meeting counters start at zero)
+        self.ver_ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
         self.ver_ws_bytes = nb
 
     # ------------------------------------------------------------------ prepared calls
