@@ -196,6 +196,12 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * fell within 1e-9 of a running-sum boundary).
  * A bad token or missing draft row raises a SPEC_DEV_* bit and the sequence
  * accepts nothing (acc_len 0, next_token = argmax p_0).
+ * Workgroups that meet (P > 1 per sequence in the rejection modes, the greedy
+ * walk) form a grid sized to be resident on the device at once, and it expects
+ * the CUs free to take it; SPEC_COOPERATIVE_LAUNCH=1 in the environment launches
+ * such grids cooperatively instead (guaranteed residency, some 17 us slower per
+ * call).  A meeting that cannot complete ends at its wait bound and raises
+ * SPEC_DEV_SYNC_TIMEOUT.
  * ws: spec_verify_workspace_size() bytes (no initial contents needed, except in
  * SPEC_GREEDY_WALK: zero-filled before the first call, see above).  Calls
  * that overlap in time must not share a workspace.

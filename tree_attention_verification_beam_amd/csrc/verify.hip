@@ -23,8 +23,8 @@
 //             tagged slots (cleared by k_vstats): every 64-bit slot word holds
 //             one 32-bit half of a value beside the exchange's round number,
 //             so a reader needs no separate arrival count.  Every workgroup
-//             then holds the same totals and takes the same decisions.  Such
-//             launches are cooperative, so all workgroups are resident; every
+//             then holds the same totals and takes the same decisions.  The
+//             grid is sized to be resident at once (occupancy query) and every
 //             wait is bounded.
 #include "common.hpp"
 
@@ -1202,7 +1202,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   void* args[] = {&A};
   hipError_t e;
   if (A.P > 1)
-    e = hipLaunchCooperativeKernel(fn, grid, dim3(kSelThreads), args, 0, s);
+    e = launch_meeting_kernel(fn, grid, dim3(kSelThreads), args, s);
   else
     e = hipLaunchKernel(fn, grid, dim3(kSelThreads), args, 0, s);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;

@@ -26,8 +26,8 @@
 // the last one resets both counters, so each call leaves its workspace ready
 // for the next (it must be zero before the first call; the entry words need
 // no clearing, as a meeting reads them only after all P have been written).
-// The launch is cooperative (every workgroup resident) and every wait is
-// bounded.
+// The grid is sized to be resident at once (occupancy query) and every wait
+// is bounded.
 //
 // A slice scan keeps two batches of 16-byte buffer loads in flight; loads past
 // the slice end return zeros and are masked to -inf.  The logits of the tested
@@ -471,7 +471,7 @@ int launch_verify_walk(int B, int T_cap, int V, const float* tgt, const int32_t*
   const dim3 grid((unsigned)(B * P));
   hipError_t e;
   if (P > 1)
-    e = hipLaunchCooperativeKernel(fn, grid, dim3(kWalkThreads), args, 0, s);
+    e = launch_meeting_kernel(fn, grid, dim3(kWalkThreads), args, s);
   else
     e = hipLaunchKernel(fn, grid, dim3(kWalkThreads), args, 0, s);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
