@@ -209,6 +209,27 @@ def verify_greedy_walk(tgt: np.ndarray, n_nodes, parent, token, depth):
     return out
 
 
+def beam_topk(logp: np.ndarray, beam_score, K_out: int, hist=None):
+    """One beam-search pruning step; see orc_beam_topk in oracle.c.
+    logp [B][K_in][V] fp32, beam_score [B][K_in] or None, hist [B][K_in][len] or None."""
+    logp = np.ascontiguousarray(logp, dtype=np.float32)
+    B, K_in, V = logp.shape
+    out = dict(parent=np.zeros((B, K_out), np.int32), token=np.zeros((B, K_out), np.int32),
+               score=np.zeros((B, K_out), np.float32))
+    length = 0
+    if hist is not None:
+        hist = _i32(hist)
+        length = hist.shape[2]
+        out["hist"] = np.zeros((B, K_out, length + 1), np.int32)
+    bs = None if beam_score is None else np.ascontiguousarray(beam_score, dtype=np.float32)
+    f = lib().orc_beam_topk
+    f.restype = ctypes.c_int
+    rc = f(B, K_in, K_out, V, _p(logp), _p(bs), _p(out["parent"]), _p(out["token"]),
+           _p(out["score"]), _p(hist), length, _p(out.get("hist")))
+    _check(rc, "beam_topk")
+    return out
+
+
 def residual_chain(p: np.ndarray, q: np.ndarray, K: int, literal: bool = False):
     """Residual distributions after 0..K rejections: (dist [K+1][V], mass [K+1], filled)."""
     p = np.ascontiguousarray(p, dtype=np.float64)

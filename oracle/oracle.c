@@ -739,3 +739,70 @@ int orc_kv_compact(int elem_bytes, int B, int Hkv, int D, int cap, int T_cap, ui
     free(tmp);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 5. Beam search pruning                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* One candidate of the pruning step: its score and its index j * V + v in the
+ * flattened (beam, token) grid. */
+typedef struct {
+    float s;
+    long idx;
+} orc_cand;
+
+/* Descending score; equal scores keep the lower flattened index first. */
+static int orc_cand_cmp(const void *a, const void *b)
+{
+    const orc_cand *x = (const orc_cand *)a, *y = (const orc_cand *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->idx > y->idx) - (x->idx < y->idx);
+}
+
+/*
+ * Scoring and pruning of one beam-search step ([ReDrafter] section "Beam Search
+ * During Inference", steps 1 and 3): every extension of beam j by token v gets
+ * the cumulative log-probability score[j] + logp[j][v] (fp32, the precision
+ * the selection is taken in), and the K_out best of the K_in * V extensions
+ * become the next beams.  Ties go to the lower flattened index j * V + v (the
+ * pages name no tie rule).  beam_score NULL means all zero (the first step,
+ * with one row).  Outputs per sequence, best first: parent beam, token, score.
+ * When hist_in is given ([B][K_in][len] token histories), hist_out
+ * [B][K_out][len + 1] gets the parent's history followed by the new token.
+ * All candidates are sorted in full; a library sort serves as the step.
+ */
+int orc_beam_topk(int B, int K_in, int K_out, int V, const float *logp, const float *beam_score,
+                  int32_t *out_parent, int32_t *out_token, float *out_score,
+                  const int32_t *hist_in, int len, int32_t *hist_out)
+{
+    if (B < 0 || K_in < 1 || V < 1 || K_out < 1 || (long)K_out > (long)K_in * V) return ORC_ERR;
+    const long n = (long)K_in * V;
+    orc_cand *c = (orc_cand *)malloc(sizeof(orc_cand) * (size_t)n);
+    if (!c) return ORC_ERR;
+    for (int b = 0; b < B; ++b) {
+        for (int j = 0; j < K_in; ++j) {
+            const float base = beam_score ? beam_score[(size_t)b * K_in + j] : 0.0f;
+            const float *row = logp + ((size_t)b * K_in + j) * (size_t)V;
+            for (int v = 0; v < V; ++v) {
+                c[(long)j * V + v].s = base + row[v];
+                c[(long)j * V + v].idx = (long)j * V + v;
+            }
+        }
+        qsort(c, (size_t)n, sizeof(orc_cand), orc_cand_cmp);
+        for (int k = 0; k < K_out; ++k) {
+            const int j = (int)(c[k].idx / V), v = (int)(c[k].idx % V);
+            out_parent[(size_t)b * K_out + k] = j;
+            out_token[(size_t)b * K_out + k] = v;
+            out_score[(size_t)b * K_out + k] = c[k].s;
+            if (hist_in && hist_out) {
+                const int32_t *src = hist_in + ((size_t)b * K_in + j) * (size_t)len;
+                int32_t *dst = hist_out + ((size_t)b * K_out + k) * (size_t)(len + 1);
+                for (int i = 0; i < len; ++i) dst[i] = src[i];
+                dst[len] = v;
+            }
+        }
+    }
+    free(c);
+    return ORC_OK;
+}
