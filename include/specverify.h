@@ -52,6 +52,7 @@ extern "C" {
 #endif
 
 #define SPEC_MAX_TREE 128 /* largest T_cap (root included) */
+#define SPEC_MAX_BEAM_TOPK 16 /* largest K_out of spec_beam_topk */
 
 typedef enum {
     SPEC_OK = 0,
@@ -235,6 +236,32 @@ int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, cons
 int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int T_cap, void *k_cache,
                     void *v_cache, int32_t *ctx_len, const int32_t *acc_len,
                     const int32_t *acc_path, int32_t *status, void *stream);
+
+/*
+ * spec_beam_topk -- the pruning step of beam search, feeding spec_build_tree.
+ *
+ * [ReDrafter] section "Beam Search During Inference", steps 1 and 3: every
+ * extension of beam j by token v scores score[j] + logp[j][v] (the cumulative
+ * log-probability; an fp32 sum), and the K_out best of the K_in * V
+ * extensions become the next beams, best first.  Equal scores go to the lower
+ * flattened index j * V + v (the pages name no tie rule); -0.0 counts as +0.0,
+ * and NaN scores have no defined place.
+ * logp [B][K_in][V] fp32 (device); beam_score [B][K_in] fp32, or NULL for all
+ * zero (the first step, K_in = 1).  Outputs [B][K_out]: out_parent (beam j),
+ * out_token (v), out_score (the sum).  hist_out [B][K_out][hist_len + 1]
+ * (NULL: no histories) gets each new beam's history, its parent's from
+ * hist_in [B][K_in][hist_len] (NULL allowed when hist_len is 0) followed by
+ * its token -- after L steps the [B][W][L] beams input of spec_build_tree.
+ * Requires 1 <= K_out <= SPEC_MAX_BEAM_TOPK and K_out <= K_in * V
+ * (SPEC_ERR_CAPACITY otherwise) and K_in * V < 2^31 (SPEC_ERR_UNSUPPORTED).
+ * ws: spec_beam_topk_workspace_size() bytes (no initial contents needed).
+ * Calls that overlap in time must not share a workspace.
+ */
+size_t spec_beam_topk_workspace_size(int B, int K_in, int K_out, int V);
+int spec_beam_topk(int B, int K_in, int K_out, int V, const float *logp, const float *beam_score,
+                   int32_t *out_parent, int32_t *out_token, float *out_score,
+                   const int32_t *hist_in, int hist_len, int32_t *hist_out, void *ws,
+                   size_t ws_bytes, void *stream);
 
 /*
  * spec_copy_probe -- plain streaming copy of n_bytes (multiple of 16) from src

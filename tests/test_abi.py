@@ -31,9 +31,10 @@ def lib():
     return binding
 
 
-def test_header_lists_the_four_calls():
+def test_header_lists_the_calls():
     d = declared()
-    for name in ("spec_build_tree", "spec_tree_attention", "spec_verify", "spec_kv_compact"):
+    for name in ("spec_build_tree", "spec_tree_attention", "spec_verify", "spec_kv_compact",
+                 "spec_beam_topk"):
         assert name in d
 
 
@@ -53,6 +54,23 @@ def test_host_only_calls(lib):
     assert cdll.spec_verify_workspace_size(0, 64, 17, 128000, 0) > 0
     assert cdll.spec_tree_attention_workspace_size(1, 64, 17, 32, 32, 128, 1024) == 0
     assert cdll.spec_tree_attention_workspace_size(1, 4, 49, 32, 8, 128, 32768) > 0
+    assert cdll.spec_beam_topk_workspace_size(1, 8, 8, 32000) > 0
+    assert cdll.spec_beam_topk_workspace_size(1, 8, 17, 32000) == 0
+
+
+def test_beam_topk_rejects_before_launch(lib):
+    cdll = lib.load()
+    # K_out beyond the limit or beyond K_in * V, and mismatched history buffers
+    assert cdll.spec_beam_topk(1, 8, 17, 32000, 16, None, 16, 16, 16, None, 0, None, 16,
+                               1 << 20, None) == -3
+    assert cdll.spec_beam_topk(1, 1, 6, 5, 16, None, 16, 16, 16, None, 0, None, 16,
+                               1 << 20, None) == -3
+    assert cdll.spec_beam_topk(1, 2, 2, 8, 16, None, 16, 16, 16, 16, 3, None, 16,
+                               1 << 20, None) == -1
+    assert cdll.spec_beam_topk(1, 2, 2, 8, 16, None, 16, 16, 16, None, 0, None, None, 0,
+                               None) == -4
+    assert cdll.spec_beam_topk(0, 2, 2, 8, None, None, None, None, None, None, 0, None, None,
+                               0, None) == 0
 
 
 def test_validation_rejects_before_launch(lib):

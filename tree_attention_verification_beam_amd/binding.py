@@ -37,6 +37,8 @@ SIGNATURES = {
     "spec_verify_workspace_size": (_c_size, [_c_int] * 5),
     "spec_verify": (_c_int, [_c_int] * 5 + [_vp] * 17 + [_c_size, _vp, _vp]),
     "spec_kv_compact": (_c_int, [_c_int] * 6 + [_vp] * 7),
+    "spec_beam_topk_workspace_size": (_c_size, [_c_int] * 4),
+    "spec_beam_topk": (_c_int, [_c_int] * 4 + [_vp] * 6 + [_c_int, _vp, _vp, _c_size, _vp]),
     "spec_copy_probe": (_c_int, [_vp, _vp, _c_size, _vp]),
 }
 
@@ -135,6 +137,18 @@ def spec_kv_compact(dt, B, Hkv, D, cache_cap, T_cap, k_cache, v_cache, ctx_len, 
                                 _ptr(ctx_len), _ptr(acc_len), _ptr(acc_path), _ptr(status),
                                 _stream(stream))
     _check("spec_kv_compact", rc)
+
+
+def spec_beam_topk_workspace_size(B, K_in, K_out, V) -> int:
+    return load().spec_beam_topk_workspace_size(B, K_in, K_out, V)
+
+
+def spec_beam_topk(B, K_in, K_out, V, logp, beam_score, out_parent, out_token, out_score,
+                   hist_in=None, hist_len=0, hist_out=None, ws=None, ws_bytes=0, stream=None):
+    rc = load().spec_beam_topk(B, K_in, K_out, V, _ptr(logp), _ptr(beam_score), _ptr(out_parent),
+                               _ptr(out_token), _ptr(out_score), _ptr(hist_in), hist_len,
+                               _ptr(hist_out), _ptr(ws), ws_bytes, _stream(stream))
+    _check("spec_beam_topk", rc)
 
 
 def spec_copy_probe(src, dst, n_bytes, stream=None):
