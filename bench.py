@@ -280,11 +280,52 @@ def main():
         },
         "device_status": status,
     }
+    if wl.tree == "beams":
+        line["beam_topk"] = time_beam_topk(torch, sv, wl)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(first, mode, args.cpu_sample_s)
     print(json.dumps(line), flush=True)
+
+
+def time_beam_topk(torch, sv, wl):
+    """The beam-search pruning step at the workload's beam shape (W beams of V
+    tokens per sequence, keep W), outside the timed step: synthetic
+    log-softmax rows of N(0, 3^2) logits, rotated over sets that exceed the
+    Infinity Cache, HIP events on the launch stream."""
+    B, K, V = wl.B, wl.W, wl.V
+    dev = torch.device("cuda:0")
+    row_bytes = B * K * V * 4
+    n_sets = max(2, min(64, (600 << 20) // row_bytes))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    sets = []
+    for _ in range(n_sets):
+        x = 3.0 * torch.randn(B, K, V, device=dev, generator=gen)
+        sets.append((torch.log_softmax(x, dim=-1).contiguous(),
+                     torch.randn(B, K, device=dev, generator=gen)))
+    par = torch.empty(B, K, dtype=torch.int32, device=dev)
+    tok = torch.empty_like(par)
+    sc = torch.empty(B, K, dtype=torch.float32, device=dev)
+    nb = sv.spec_beam_topk_workspace_size(B, K, K, V)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+    calls = [sv.prepare("spec_beam_topk", B, K, K, V, lp, bs, par, tok, sc, None, 0, None, ws, nb)
+             for lp, bs in sets]
+    for i in range(5):
+        calls[i % n_sets]()
+    torch.cuda.synchronize()
+    n = 50
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        calls[i % n_sets]()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return {"shape": {"B": B, "beams": K, "V": V, "keep": K}, "avg_call_us": us,
+            "algorithmic_bytes": row_bytes, "GBps": row_bytes / (us * 1e-6) / 1e9}
 
 
 def cpu_baseline(inp, mode, budget_s):

@@ -79,13 +79,35 @@ __device__ inline void tl_pop(TopList<KM>& t) {
   t.k[KM - 1] = 0;
 }
 
+// Wave maximum of a 32-bit value, uniform in every lane: a running maximum
+// along each 16-lane row by DPP row shifts (a lane whose source lies outside
+// its row keeps its own value), then the four rows' last lanes.  A few cycles
+// per step, where a shuffle is an LDS-crossbar round trip.
+__device__ inline uint32_t wave_max_u32(uint32_t v) {
+  uint32_t w;
+  w = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v = w > v ? w : v;
+  w = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v = w > v ? w : v;
+  w = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v = w > v ? w : v;
+  w = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v = w > v ? w : v;
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+  const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+  return ab > cd ? ab : cd;
+}
+
+// Wave maximum of a 64-bit key: the high halves first, then the low halves of
+// the lanes holding the highest high half.
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  const uint32_t hi = (uint32_t)(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? (uint32_t)v : 0u);
+  return ((uint64_t)mh << 32) | ml;
 }
 
 // The workgroup's best n (<= KM) keys, in order, into out[0..n) (LDS), from
