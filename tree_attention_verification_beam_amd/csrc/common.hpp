@@ -38,22 +38,73 @@ __device__ inline uint64_t load_coherent(const uint64_t* p) {
 __device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------- reductions
+// Cross-lane exchanges without the LDS crossbar: within a 16-lane row, DPP
+// quad permutes (partner l ^ 1, l ^ 2) and row mirrors (partner 7 - l within
+// each half-row, then 15 - l within the row); across rows, gfx950's
+// v_permlane16_swap / v_permlane32_swap (partner l ^ 16, l ^ 32).  Each step
+// pairs lanes whose partial results cover disjoint lane sets, so five steps
+// leave every lane with the whole wave's combination, and partners compute
+// the same value (the combining operations are commutative), so the result is
+// identical in every lane.  Every lane of the wave must be active.
+template <int STEP>
+__device__ inline uint32_t lane_partner(uint32_t v) {
+  if constexpr (STEP == 0) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);  // quad 1,0,3,2
+  } else if constexpr (STEP == 1) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);  // quad 2,3,0,1
+  } else if constexpr (STEP == 2) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);  // half mirror
+  } else if constexpr (STEP == 3) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);  // row mirror
+  } else if constexpr (STEP == 4) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return ((__lane_id() >> 4) & 1) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (__lane_id() >> 5) ? r[0] : r[1];
+  }
+}
+
+template <int STEP>
+__device__ inline float partner_f32(float v) {
+  return __uint_as_float(lane_partner<STEP>(__float_as_uint(v)));
+}
+template <int STEP>
+__device__ inline int partner_i32(int v) {
+  return (int)lane_partner<STEP>((uint32_t)v);
+}
+template <int STEP>
+__device__ inline double partner_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = lane_partner<STEP>((uint32_t)b), hi = lane_partner<STEP>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
 __device__ inline float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, partner_f32<0>(v));
+  v = fmaxf(v, partner_f32<1>(v));
+  v = fmaxf(v, partner_f32<2>(v));
+  v = fmaxf(v, partner_f32<3>(v));
+  v = fmaxf(v, partner_f32<4>(v));
+  return fmaxf(v, partner_f32<5>(v));
 }
 
 __device__ inline double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += partner_f64<0>(v);
+  v += partner_f64<1>(v);
+  v += partner_f64<2>(v);
+  v += partner_f64<3>(v);
+  v += partner_f64<4>(v);
+  return v + partner_f64<5>(v);
 }
 
 __device__ inline float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += partner_f32<0>(v);
+  v += partner_f32<1>(v);
+  v += partner_f32<2>(v);
+  v += partner_f32<3>(v);
+  v += partner_f32<4>(v);
+  return v + partner_f32<5>(v);
 }
 
 // (value, index) maximum: larger value wins; equal values keep the lower index.
@@ -64,13 +115,20 @@ __device__ inline void argmax_merge(float& m, int& a, float m2, int a2) {
   }
 }
 
+template <int STEP>
+__device__ inline void argmax_step(float& m, int& a) {
+  const float m2 = partner_f32<STEP>(m);
+  const int a2 = partner_i32<STEP>(a);
+  argmax_merge(m, a, m2, a2);
+}
+
 __device__ inline void wave_argmax(float& m, int& a) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float m2 = __shfl_xor(m, o, kWave);
-    int a2 = __shfl_xor(a, o, kWave);
-    argmax_merge(m, a, m2, a2);
-  }
+  argmax_step<0>(m, a);
+  argmax_step<1>(m, a);
+  argmax_step<2>(m, a);
+  argmax_step<3>(m, a);
+  argmax_step<4>(m, a);
+  argmax_step<5>(m, a);
 }
 
 // ---------------------------------------------------------------- host side

@@ -485,8 +485,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       // the row maximum moves only when some lane outgrew it by 2^kRescale;
       // then the 4 lane groups holding the row agree on the new maximum
       if (__builtin_amdgcn_ballot_w64(lmax > m_run[i] + kRescale) != 0ull) {
-        float tmax = fmaxf(lmax, __shfl_xor(lmax, 16, kWave));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, kWave));
+        float tmax = fmaxf(lmax, partner_f32<4>(lmax));  // lane l ^ 16
+        tmax = fmaxf(tmax, partner_f32<5>(tmax));        // lane l ^ 32
         const float m_new = fmaxf(m_run[i], tmax);
         const float alpha =
             (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
@@ -570,8 +570,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // the 4 lane groups of a query hold partial sums over their own keys
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
-    l_run[i] += __shfl_xor(l_run[i], 16, kWave);
-    l_run[i] += __shfl_xor(l_run[i], 32, kWave);
+    l_run[i] += partner_f32<4>(l_run[i]);
+    l_run[i] += partner_f32<5>(l_run[i]);
   }
 
   // ---------------------------------------------------------------- combine key groups
