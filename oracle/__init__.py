@@ -230,6 +230,21 @@ def beam_topk(logp: np.ndarray, beam_score, K_out: int, hist=None):
     return out
 
 
+def select_tree(cand_parent, cand_token, cand_logp, N_keep: int):
+    """Dynamic tree selection under a node budget; see orc_select_tree in oracle.c."""
+    cand_parent, cand_token = _i32(cand_parent), _i32(cand_token)
+    cand_logp = np.ascontiguousarray(cand_logp, dtype=np.float32)
+    B, N = cand_parent.shape
+    out = dict(parent=np.zeros((B, N_keep), np.int32), token=np.zeros((B, N_keep), np.int32),
+               src=np.zeros((B, N_keep), np.int32), score=np.zeros((B, N_keep), np.float32))
+    f = lib().orc_select_tree
+    f.restype = ctypes.c_int
+    rc = f(B, N, N_keep, _p(cand_parent), _p(cand_token), _p(cand_logp), _p(out["parent"]),
+           _p(out["token"]), _p(out["src"]), _p(out["score"]))
+    _check(rc, "select_tree")
+    return out
+
+
 def residual_chain(p: np.ndarray, q: np.ndarray, K: int, literal: bool = False):
     """Residual distributions after 0..K rejections: (dist [K+1][V], mass [K+1], filled)."""
     p = np.ascontiguousarray(p, dtype=np.float64)

@@ -806,3 +806,85 @@ int orc_beam_topk(int B, int K_in, int K_out, int V, const float *logp, const fl
     free(c);
     return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 6. Dynamic tree selection                                                 */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    float s;
+    int i;
+} orc_node_score;
+
+static int orc_node_cmp(const void *a, const void *b)
+{
+    const orc_node_score *x = (const orc_node_score *)a, *y = (const orc_node_score *)b;
+    if (x->s > y->s) return -1;
+    if (x->s < y->s) return 1;
+    return (x->i > y->i) - (x->i < y->i);
+}
+
+/*
+ * Dynamic draft-tree selection under a node budget ([Drafters] page, the
+ * EAGLE-2 paragraph: a branch is scored by the product of the drafter's
+ * confidences along its path from the root, and the highest-scoring ones are
+ * kept; [Clover] sizes its tree by a node budget).  Candidate i is node i + 1
+ * with parent node cand_parent[i] in [0, i] (0 = root), token cand_token[i]
+ * and log-confidence cand_logp[i] <= 0.  In log form the path score is
+ * S(root) = 0, S(node) = S(parent) + logp, an fp32 sum taken from the root
+ * down.  The N_keep candidates with the highest S are kept, the lower index on
+ * ties; since logp <= 0 a parent scores at least as high as its child and has
+ * the lower index, so the kept set holds every kept node's parent.  Output per
+ * sequence: the kept candidates in their original order as an explicit
+ * candidate list -- kept candidate k is node k + 1, keep_parent[k] the new
+ * number of its parent node (0 = root) -- with keep_token, keep_src (original
+ * candidate index) and keep_score (S).  Invalid input (a parent out of range,
+ * logp > 0 or NaN) returns ORC_ERR.
+ */
+int orc_select_tree(int B, int N, int N_keep, const int32_t *cand_parent,
+                    const int32_t *cand_token, const float *cand_logp, int32_t *keep_parent,
+                    int32_t *keep_token, int32_t *keep_src, float *keep_score)
+{
+    if (B < 0 || N < 1 || N_keep < 1 || N_keep > N) return ORC_ERR;
+    float *S = (float *)malloc(sizeof(float) * (size_t)(N + 1));
+    orc_node_score *ns = (orc_node_score *)malloc(sizeof(orc_node_score) * (size_t)N);
+    int *kept = (int *)malloc(sizeof(int) * (size_t)N);
+    int *newnode = (int *)malloc(sizeof(int) * (size_t)(N + 1));
+    if (!S || !ns || !kept || !newnode) {
+        free(S); free(ns); free(kept); free(newnode);
+        return ORC_ERR;
+    }
+    int rc = ORC_OK;
+    for (int b = 0; b < B && rc == ORC_OK; ++b) {
+        const int32_t *par = cand_parent + (size_t)b * N;
+        const int32_t *tok = cand_token + (size_t)b * N;
+        const float *lp = cand_logp + (size_t)b * N;
+        S[0] = 0.0f;
+        for (int i = 0; i < N; ++i) {
+            if (par[i] < 0 || par[i] > i || !(lp[i] <= 0.0f)) { rc = ORC_ERR; break; }
+            S[i + 1] = S[par[i]] + lp[i]; /* the parent node precedes node i + 1 */
+        }
+        if (rc != ORC_OK) break;
+        for (int i = 0; i < N; ++i) {
+            ns[i].s = S[i + 1];
+            ns[i].i = i;
+            kept[i] = 0;
+        }
+        qsort(ns, (size_t)N, sizeof(orc_node_score), orc_node_cmp);
+        for (int k = 0; k < N_keep; ++k) kept[ns[k].i] = 1;
+        newnode[0] = 0;
+        int k = 0;
+        for (int i = 0; i < N; ++i) {
+            if (!kept[i]) continue;
+            if (par[i] > 0 && !kept[par[i] - 1]) { rc = ORC_ERR; break; } /* cannot happen */
+            newnode[i + 1] = k + 1;
+            keep_parent[(size_t)b * N_keep + k] = newnode[par[i]];
+            keep_token[(size_t)b * N_keep + k] = tok[i];
+            keep_src[(size_t)b * N_keep + k] = i;
+            keep_score[(size_t)b * N_keep + k] = S[i + 1];
+            ++k;
+        }
+    }
+    free(S); free(ns); free(kept); free(newnode);
+    return rc;
+}
