@@ -53,6 +53,7 @@ extern "C" {
 
 #define SPEC_MAX_TREE 128 /* largest T_cap (root included) */
 #define SPEC_MAX_BEAM_TOPK 16 /* largest K_out of spec_beam_topk */
+#define SPEC_MAX_SELECT 1024  /* largest candidate count of spec_select_tree */
 
 typedef enum {
     SPEC_OK = 0,
@@ -262,6 +263,34 @@ int spec_beam_topk(int B, int K_in, int K_out, int V, const float *logp, const f
                    int32_t *out_parent, int32_t *out_token, float *out_score,
                    const int32_t *hist_in, int hist_len, int32_t *hist_out, void *ws,
                    size_t ws_bytes, void *stream);
+
+/*
+ * spec_select_tree -- keep the best branches of a draft tree under a node budget.
+ *
+ * [Drafters] "Speculative Decoding, Part 2: A History of Drafters", the EAGLE-2
+ * paragraph: a branch scores the product of the drafter's confidences along
+ * its path from the root, the highest-scoring branches are kept, and a parent
+ * always scores at least as high as its children; [Clover] sizes its tree by
+ * a node budget.  In log form: S(root) = 0, S(node) = S(parent) + logp(node),
+ * an fp32 sum from the root down.  The N_keep candidates with the highest S
+ * are kept, the lower candidate index on ties, so every kept node's parent is
+ * kept too.
+ * Candidate i of sequence b is node i + 1: cand_parent [B][N] (its parent
+ * node, in [0, i]; 0 = root), cand_token [B][N], cand_logp [B][N] (its
+ * log-confidence, <= 0).  Outputs [B][N_keep], the kept candidates in their
+ * original order as an explicit candidate list for spec_build_tree (kept
+ * candidate k is node k + 1): keep_parent (the new number of its parent node),
+ * keep_token, keep_src (original candidate index; nullable) and keep_score
+ * (S; nullable).  A sequence with a parent out of range, logp > 0 or NaN gets
+ * keep_parent = -1 (spec_build_tree then makes it a root-only tree) and
+ * raises SPEC_DEV_BAD_PARENT.
+ * Requires 1 <= N_keep <= N <= SPEC_MAX_SELECT and N_keep < SPEC_MAX_TREE.
+ * No workspace.
+ */
+int spec_select_tree(int B, int N, int N_keep, const int32_t *cand_parent,
+                     const int32_t *cand_token, const float *cand_logp, int32_t *keep_parent,
+                     int32_t *keep_token, int32_t *keep_src, float *keep_score, int32_t *status,
+                     void *stream);
 
 /*
  * spec_copy_probe -- plain streaming copy of n_bytes (multiple of 16) from src

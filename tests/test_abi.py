@@ -34,7 +34,7 @@ def lib():
 def test_header_lists_the_calls():
     d = declared()
     for name in ("spec_build_tree", "spec_tree_attention", "spec_verify", "spec_kv_compact",
-                 "spec_beam_topk"):
+                 "spec_beam_topk", "spec_select_tree"):
         assert name in d
 
 
@@ -56,6 +56,16 @@ def test_host_only_calls(lib):
     assert cdll.spec_tree_attention_workspace_size(1, 4, 49, 32, 8, 128, 32768) > 0
     assert cdll.spec_beam_topk_workspace_size(1, 8, 8, 32000) > 0
     assert cdll.spec_beam_topk_workspace_size(1, 8, 17, 32000) == 0
+
+
+def test_select_tree_rejects_before_launch(lib):
+    cdll = lib.load()
+    args = [16] * 7 + [None, 16]
+    assert cdll.spec_select_tree(1, 10, 11, *args) == -1      # budget above the candidates
+    assert cdll.spec_select_tree(1, 2000, 8, *args) == -3     # too many candidates
+    assert cdll.spec_select_tree(1, 300, 128, *args) == -3    # budget beyond a tree
+    assert cdll.spec_select_tree(1, 10, 4, None, *args[1:]) == -1
+    assert cdll.spec_select_tree(0, 10, 4, *([None] * 9)) == 0
 
 
 def test_beam_topk_rejects_before_launch(lib):

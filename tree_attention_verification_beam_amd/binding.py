@@ -39,6 +39,7 @@ SIGNATURES = {
     "spec_kv_compact": (_c_int, [_c_int] * 6 + [_vp] * 7),
     "spec_beam_topk_workspace_size": (_c_size, [_c_int] * 4),
     "spec_beam_topk": (_c_int, [_c_int] * 4 + [_vp] * 6 + [_c_int, _vp, _vp, _c_size, _vp]),
+    "spec_select_tree": (_c_int, [_c_int] * 3 + [_vp] * 9),
     "spec_copy_probe": (_c_int, [_vp, _vp, _c_size, _vp]),
 }
 
@@ -149,6 +150,14 @@ def spec_beam_topk(B, K_in, K_out, V, logp, beam_score, out_parent, out_token, o
                                _ptr(out_token), _ptr(out_score), _ptr(hist_in), hist_len,
                                _ptr(hist_out), _ptr(ws), ws_bytes, _stream(stream))
     _check("spec_beam_topk", rc)
+
+
+def spec_select_tree(B, N, N_keep, cand_parent, cand_token, cand_logp, keep_parent, keep_token,
+                     keep_src=None, keep_score=None, status=None, stream=None):
+    rc = load().spec_select_tree(B, N, N_keep, _ptr(cand_parent), _ptr(cand_token),
+                                 _ptr(cand_logp), _ptr(keep_parent), _ptr(keep_token),
+                                 _ptr(keep_src), _ptr(keep_score), _ptr(status), _stream(stream))
+    _check("spec_select_tree", rc)
 
 
 def spec_copy_probe(src, dst, n_bytes, stream=None):
