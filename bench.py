@@ -282,6 +282,8 @@ def main():
     }
     if wl.tree == "beams":
         line["beam_topk"] = time_beam_topk(torch, sv, wl)
+    if wl.tree == "static":
+        line["select_tree"] = time_select_tree(torch, sv, wl)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu_baseline:
@@ -326,6 +328,49 @@ def time_beam_topk(torch, sv, wl):
     us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
     return {"shape": {"B": B, "beams": K, "V": V, "keep": K}, "avg_call_us": us,
             "algorithmic_bytes": row_bytes, "GBps": row_bytes / (us * 1e-6) / 1e9}
+
+
+def time_select_tree(torch, sv, wl):
+    """Dynamic tree selection at the parallel-head workload's shape, outside the
+    timed step: per sequence a candidate tree expanded with fan-outs 8, 4, 4, 2
+    (424 candidates) with log-confidences of N(0, 3^2) softmax rows, cut to the
+    workload's 16-node budget; HIP events on the launch stream."""
+    B, keep = wl.B, wl.T_cap - 1
+    rng = np.random.default_rng(78)
+    par, nodes = [], [0]
+    for fan in (8, 4, 4, 2):
+        nxt = []
+        for p in nodes:
+            for _ in range(fan):
+                par.append(p)
+                nxt.append(len(par))
+        nodes = nxt
+    N = len(par)
+    logits = 3.0 * rng.standard_normal((B, N))
+    lp = logits - np.log(np.exp(logits).sum(axis=1, keepdims=True))  # confidences < 1
+    dev = torch.device("cuda:0")
+    t_par = torch.tensor(np.tile(np.array(par, np.int32), (B, 1)), device=dev)
+    t_tok = torch.tensor(rng.integers(0, wl.V, size=(B, N)).astype(np.int32), device=dev)
+    t_lp = torch.tensor(lp.astype(np.float32), device=dev)
+    outs = [torch.empty(B, keep, dtype=torch.int32, device=dev) for _ in range(3)]
+    score = torch.empty(B, keep, dtype=torch.float32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    call = sv.prepare("spec_select_tree", B, N, keep, t_par, t_tok, t_lp, outs[0], outs[1],
+                      outs[2], score, status)
+    for _ in range(5):
+        call()
+    torch.cuda.synchronize()
+    n = 50
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record()
+        call()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    return {"shape": {"B": B, "candidates": N, "keep": keep}, "avg_call_us": us,
+            "device_status": int(status.item())}
 
 
 def cpu_baseline(inp, mode, budget_s):

@@ -14,7 +14,8 @@
 // k_select_tree: one workgroup per sequence, everything in LDS.  Scores are
 // computed level by level (a node is summed in the round after its parent),
 // so each sum happens in the same order as the definition; the rank of a node
-// is the number of nodes ahead of it (a broadcast LDS read per comparison);
+// is the number of nodes ahead of it (broadcast 16-byte LDS reads of the
+// scores, sixteen comparisons per iteration);
 // kept nodes are numbered by a ballot scan in node order.
 #include "common.hpp"
 
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(kSelTreeThreads) void k_select_tree(
     int32_t* __restrict__ keep_parent, int32_t* __restrict__ keep_token,
     int32_t* __restrict__ keep_src, float* __restrict__ keep_score, int32_t* status) {
   __shared__ float s_S[SPEC_MAX_SELECT + 1];    // path score of node n (node 0 = root)
+  __shared__ __align__(16) float s_C[SPEC_MAX_SELECT];  // score of candidate u, -inf padded
   __shared__ int s_round[SPEC_MAX_SELECT + 1];  // round in which node n was scored, -1 not yet
   __shared__ int s_par[SPEC_MAX_SELECT];
   __shared__ int s_new[SPEC_MAX_SELECT];        // new node number of candidate i (0: dropped)
@@ -87,17 +89,31 @@ __global__ __launch_bounds__(kSelTreeThreads) void k_select_tree(
     }
 
     // ---------------------------------------------------------------- rank
+    // candidate scores in a -inf-padded copy read 16 at a time (a padded entry
+    // u >= N never counts: -inf is never ahead, and on a tie u > i)
+    const int n_pad = (N + 15) & ~15;
+    for (int u = tid; u < n_pad; u += kSelTreeThreads) s_C[u] = u < N ? s_S[u + 1] : -INFINITY;
+    __syncthreads();
     bool keep[kPerThread];
 #pragma unroll
     for (int r = 0; r < kPerThread; ++r) {
       const int i = r * kSelTreeThreads + tid;
       keep[r] = false;
       if (i < N) {
-        const float si = s_S[i + 1];
+        const float si = s_C[i];
         int ahead = 0;
-        for (int u = 0; u < N; ++u) {
-          const float su = s_S[u + 1];
-          ahead += (su > si || (su == si && u < i)) ? 1 : 0;
+        for (int u0 = 0; u0 < n_pad; u0 += 16) {
+          f32x4 c[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(s_C + u0 + 4 * q);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float su = c[q][e];
+              const int u = u0 + 4 * q + e;
+              ahead += (su > si || (su == si && u < i)) ? 1 : 0;
+            }
         }
         keep[r] = ahead < N_keep;
       }
