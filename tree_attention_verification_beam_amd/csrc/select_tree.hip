@@ -14,8 +14,8 @@
 // k_select_tree: one workgroup per sequence, everything in LDS.  Scores are
 // computed level by level (a node is summed in the round after its parent),
 // so each sum happens in the same order as the definition; the rank of a node
-// is the number of nodes ahead of it (broadcast 16-byte LDS reads of the
-// scores, sixteen comparisons per iteration);
+// is the number of nodes ahead of it (one 64-bit key per node, read from LDS
+// two at a time, one compare each);
 // kept nodes are numbered by a ballot scan in node order.
 #include "common.hpp"
 
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(kSelTreeThreads) void k_select_tree(
     int32_t* __restrict__ keep_parent, int32_t* __restrict__ keep_token,
     int32_t* __restrict__ keep_src, float* __restrict__ keep_score, int32_t* status) {
   __shared__ float s_S[SPEC_MAX_SELECT + 1];    // path score of node n (node 0 = root)
-  __shared__ __align__(16) float s_C[SPEC_MAX_SELECT];  // score of candidate u, -inf padded
+  __shared__ __align__(16) uint64_t s_K[SPEC_MAX_SELECT];  // rank key of candidate u, 0 padded
   __shared__ int s_round[SPEC_MAX_SELECT + 1];  // round in which node n was scored, -1 not yet
   __shared__ int s_par[SPEC_MAX_SELECT];
   __shared__ int s_new[SPEC_MAX_SELECT];        // new node number of candidate i (0: dropped)
@@ -89,10 +89,21 @@ __global__ __launch_bounds__(kSelTreeThreads) void k_select_tree(
     }
 
     // ---------------------------------------------------------------- rank
-    // candidate scores in a -inf-padded copy read 16 at a time (a padded entry
-    // u >= N never counts: -inf is never ahead, and on a tie u > i)
-    const int n_pad = (N + 15) & ~15;
-    for (int u = tid; u < n_pad; u += kSelTreeThreads) s_C[u] = u < N ? s_S[u + 1] : -INFINITY;
+    // one 64-bit key per candidate, larger = ahead: the score's bits in an
+    // unsigned order above the complement of the index (a lower index wins a
+    // tie); -0.0 ranks as +0.0.  Zero pads the copy to a multiple of 8, and a
+    // zero key is never ahead.
+    const int n_pad = (N + 7) & ~7;
+    for (int u = tid; u < n_pad; u += kSelTreeThreads) {
+      uint64_t key = 0;
+      if (u < N) {
+        uint32_t bits = __float_as_uint(s_S[u + 1]);
+        if (bits == 0x80000000u) bits = 0;
+        const uint32_t o = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+        key = ((uint64_t)o << 32) | (uint64_t)(~(uint32_t)u);
+      }
+      s_K[u] = key;
+    }
     __syncthreads();
     bool keep[kPerThread];
 #pragma unroll
@@ -100,20 +111,18 @@ __global__ __launch_bounds__(kSelTreeThreads) void k_select_tree(
       const int i = r * kSelTreeThreads + tid;
       keep[r] = false;
       if (i < N) {
-        const float si = s_C[i];
+        const uint64_t ki = s_K[i];
         int ahead = 0;
-        for (int u0 = 0; u0 < n_pad; u0 += 16) {
-          f32x4 c[4];
+        for (int u0 = 0; u0 < n_pad; u0 += 8) {
+          uint64_t c[8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(s_C + u0 + 4 * q);
+          for (int q = 0; q < 4; ++q) {
+            const auto two = *reinterpret_cast<const u32x4*>(s_K + u0 + 2 * q);
+            c[2 * q] = ((uint64_t)two[1] << 32) | two[0];
+            c[2 * q + 1] = ((uint64_t)two[3] << 32) | two[2];
+          }
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float su = c[q][e];
-              const int u = u0 + 4 * q + e;
-              ahead += (su > si || (su == si && u < i)) ? 1 : 0;
-            }
+          for (int e = 0; e < 8; ++e) ahead += c[e] > ki ? 1 : 0;
         }
         keep[r] = ahead < N_keep;
       }
