@@ -200,9 +200,9 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * accepts nothing (acc_len 0, next_token = argmax p_0).
  * Workgroups that meet (P > 1 per sequence in the rejection modes, the greedy
  * walk) form a grid sized to be resident on the device at once, and it expects
- * the CUs free to take it; SPEC_COOPERATIVE_LAUNCH=1 in the environment launches
- * such grids cooperatively instead (guaranteed residency, some 17 us slower per
- * call).  A meeting that cannot complete ends at its wait bound and raises
+ * the CUs free to take it; SPEC_COOPERATIVE_LAUNCH=1 in the environment (read
+ * at each call) launches such grids cooperatively instead (guaranteed
+ * residency, some 17 us slower per call).  A meeting that cannot complete ends at its wait bound and raises
  * SPEC_DEV_SYNC_TIMEOUT.
  * ws: spec_verify_workspace_size() bytes (no initial contents needed, except in
  * SPEC_GREEDY_WALK: zero-filled before the first call, see above).  Calls

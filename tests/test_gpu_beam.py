@@ -60,7 +60,8 @@ def assert_same(res, ref, what):
 
 
 @pytest.mark.parametrize("B,K_in,V,K_out", [(2, 8, 32000, 8), (3, 1, 5001, 16), (4, 16, 1000, 16),
-                                            (2, 8, 32000, 1), (5, 2, 7, 14)])
+                                            (2, 8, 32000, 1), (5, 2, 7, 14),
+                                            (64, 4, 128000, 4)])
 def test_beam_topk_matches_oracle(gpu, B, K_in, V, K_out):
     rng = np.random.default_rng(B * 100 + K_in * 10 + K_out)
     log(f"case beam top-K B={B} K_in={K_in} V={V} K_out={K_out}")

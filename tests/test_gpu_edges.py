@@ -235,3 +235,23 @@ def plant_greedy_all(inp, tr):
             par = 0 if k == 0 else tr["beam_node"][b, 0, k - 1]
             tgt[b, par, inp["beams"][b, 0, k]] = tgt[b, par].max() + 20.0
     return tgt
+
+
+def test_meeting_kernels_launched_cooperatively(gpu, monkeypatch):
+    """SPEC_COOPERATIVE_LAUNCH=1 launches the grids whose workgroups meet (the
+    split select of the rejection modes, the greedy walk) cooperatively; the
+    results are the same as the oracle's."""
+    monkeypatch.setenv("SPEC_COOPERATIVE_LAUNCH", "1")
+    inp = synth.make_inputs(4, 303, B_override=1, ctx_override=200)
+    tr = oracle_tree(inp)
+    log("case cooperative launches: sequential rejection, greedy walk")
+    step = pipeline.Step(inp, "reject_recursive", with_kv=False)
+    res = step.run()
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    assert_verify_equal(res, oracle_verify(inp, tr, "reject_recursive"), "cooperative recursive")
+    inp1 = synth.make_inputs(1, 304)
+    tr1 = oracle_tree(inp1)
+    step = pipeline.Step(inp1, "greedy_walk", with_kv=False)
+    res = step.run()
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    assert_verify_equal(res, oracle_verify(inp1, tr1, "greedy_walk"), "cooperative walk")

@@ -142,16 +142,14 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Launch of a kernel whose workgroups meet (every workgroup must be resident;
 // the grid is sized from the occupancy query to fit the device at once).  An
 // ordinary launch is the default: a cooperative launch costs some 17 us more
-// per call on MI355X.  SPEC_COOPERATIVE_LAUNCH=1 in the environment selects the
-// cooperative launch, which also guarantees residency when other streams keep
-// CUs busy; without it a meeting that cannot complete ends at its wait bound
-// and raises SPEC_DEV_SYNC_TIMEOUT.
+// per call on MI355X.  SPEC_COOPERATIVE_LAUNCH=1 in the environment (read at
+// each call) selects the cooperative launch, which also guarantees residency
+// when other streams keep CUs busy; without it a meeting that cannot complete
+// ends at its wait bound and raises SPEC_DEV_SYNC_TIMEOUT.
 inline hipError_t launch_meeting_kernel(const void* fn, dim3 grid, dim3 block, void** args,
                                         hipStream_t s) {
-  static const bool coop = [] {
-    const char* e = getenv("SPEC_COOPERATIVE_LAUNCH");
-    return e && e[0] == '1';
-  }();
+  const char* e = getenv("SPEC_COOPERATIVE_LAUNCH");  // read per call
+  const bool coop = e && e[0] == '1';
   return coop ? hipLaunchCooperativeKernel(fn, grid, block, args, 0, s)
               : hipLaunchKernel(fn, grid, block, args, 0, s);
 }

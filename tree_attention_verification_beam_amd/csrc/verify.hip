@@ -1074,8 +1074,8 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
 // least 2048 vocabulary entries per workgroup.
 int choose_p(int mode, int B, int V) {
   if (mode == SPEC_GREEDY) return 1;
-  static int cached_capacity = -1;
-  static int cached_device = -1;
+  thread_local int cached_capacity = -1;  // per host thread: no shared state
+  thread_local int cached_device = -1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   if (cached_device != dev) {

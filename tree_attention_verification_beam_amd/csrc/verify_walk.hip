@@ -405,8 +405,8 @@ __global__ __launch_bounds__(kWalkThreads) void k_vwalk(WalkArgs A) {
 // Largest P with B * P co-resident workgroups, at most kWalkMaxP, and at least
 // 2048 vocabulary entries per workgroup.
 int choose_walk_p(int B, int V) {
-  static int cached_capacity = -1;
-  static int cached_device = -1;
+  thread_local int cached_capacity = -1;  // per host thread: no shared state
+  thread_local int cached_device = -1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   if (cached_device != dev) {
