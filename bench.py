@@ -242,6 +242,7 @@ def main():
         v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
                                     inp["dft_row"] if inp["dft_row"] is not None else None, mode,
                                     st.decision.cpu().numpy()))
+    n_accept = [int(st.acc_len.sum().item()) + st.B for _, st in steps_all]
     a_avg = float(np.mean([a_bytes[i % n_sets] for i in range(args.steps)]))
     v_avg = float(np.mean(v_bytes))
     achieved = a_avg / attn_avg_s / 1e9
@@ -279,6 +280,11 @@ def main():
                 / HBM_PEAK_GBPS,
         },
         "device_status": status,
+        # beside `value`: verified nodes per second of attention + verify time
+        # only, and accepted tokens (acc_len + 1 per sequence) per step time
+        "verified_tokens_per_s_attention_verify":
+            float(np.mean(n_draft)) / ((brk["attention"] + brk["verify"]) * 1e-6),
+        "accepted_tokens_per_s": float(np.mean(n_accept)) / (ms_per_step * 1e-3),
     }
     if wl.tree == "beams":
         line["beam_topk"] = time_beam_topk(torch, sv, wl)
