@@ -22,10 +22,12 @@
 // the P entries in the same order and takes the same decisions.  Entries of
 // meeting r sit in parity r & 1: meeting r + 2 overwrites them only after all
 // P workgroups have arrived at meeting r + 1, i.e. after every reader is done
-// with meeting r.  After the walk every workgroup adds one to an exit counter;
-// the last one resets both counters, so each call leaves its workspace ready
-// for the next (it must be zero before the first call; the entry words need
-// no clearing, as a meeting reads them only after all P have been written).
+// with meeting r.  After the last meeting the lead workgroup resets the
+// counter; a workgroup still waiting at that meeting sees it fall to or below
+// the value it had before the meeting, which only the reset can cause, and
+// takes that as completion.  So each call leaves its workspace ready for the
+// next (it must be zero before the first call; the entry words need no
+// clearing, as a meeting reads them only after all P have been written).
 // The grid is sized to be resident at once (occupancy query) and every wait
 // is bounded.
 //
@@ -51,7 +53,8 @@ constexpr int kWalkMaxP = 32;
 constexpr int kBatch = 8;  // 16-byte loads per thread per batch (two batches in flight)
 constexpr float kLog2eW = 1.4426950408889634f;
 constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3, raw 32-bit loads
-// per sequence: arrival and exit counters, then [2 parities][P][2] entry words
+// per sequence: the arrival counter (in a 64-byte header), then
+// [2 parities][P][2] entry words
 constexpr size_t kWalkStride = 64 + 2 * kWalkMaxP * 2 * 8;
 
 struct WalkArgs {
@@ -229,14 +232,22 @@ __device__ void meet(uint64_t* seq, int P, int w, int round, WalkShared& sh, int
     store_coherent(entries + 2 * w, ma);
     store_coherent(entries + 2 * w + 1, (uint64_t)__double_as_longlong(sh.S));
     wait_stores_done();
-    __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t target = (uint64_t)(round + 1) * P;
-    int spins = 0;
-    while (load_coherent(arrive) < target) {
-      __builtin_amdgcn_s_sleep(1);  // back off: P pollers share the counter's line
-      if (++spins > (1 << 22)) {
-        raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
-        break;
+    const uint64_t base = (uint64_t)round * P;  // the counter before this meeting
+    const uint64_t target = base + P;
+    const uint64_t old =
+        __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1 < target) {  // (the last to arrive does not wait)
+      int spins = 0;
+      for (;;) {
+        const uint64_t v = load_coherent(arrive);
+        // v <= base: the lead has reset the counter after the last meeting,
+        // which it does only once all P have arrived at it
+        if (v >= target || v <= base) break;
+        __builtin_amdgcn_s_sleep(1);  // back off: P pollers share the counter's line
+        if (++spins > (1 << 22)) {
+          raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
+          break;
+        }
       }
     }
   }
@@ -367,16 +378,9 @@ __global__ __launch_bounds__(kWalkThreads) void k_vwalk(WalkArgs A) {
   }
 
   // ---------------------------------------------------------------- leave
-  // the last workgroup out resets the counters (every other one is past its
-  // last meeting by then)
-  if (P > 1 && tid == 0) {
-    const uint64_t old = __hip_atomic_fetch_add(seq + 1, (uint64_t)1, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint64_t)P - 1) {
-      store_coherent(seq, 0ull);
-      store_coherent(seq + 1, 0ull);
-    }
-  }
+  // the lead resets the arrival counter: it is past the last meeting, so all P
+  // have arrived there, and one still waiting reads the reset as completion
+  if (P > 1 && lead && tid == 0) store_coherent(seq, 0ull);
   if (!lead) return;
 
   // ---------------------------------------------------------------- outputs
