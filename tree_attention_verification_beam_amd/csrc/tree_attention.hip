@@ -17,7 +17,10 @@
 // tiles through LDS (double-buffered; V stored transposed so the P V operand is
 // a contiguous LDS read), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 so
 // that each lane owns one query row, runs the online softmax in fp32 in exp2
-// form, and accumulates O^T = V^T P^T with the same MFMA.  When few rows exist
+// form, and accumulates O^T = V^T P^T with the same MFMA (and, when every wave
+// sees all keys of a tile, the row sums of P as one more MFMA against an
+// all-ones operand, which leaves the softmax only its exponentials and the
+// running maximum on the VALU).  When few rows exist
 // (no GQA, small trees) the waves split each key tile instead (KG key groups)
 // and combine through LDS at the end.  The running maximum is only moved when
 // a score exceeds it by more than 2^8, so most tiles skip the rescale of the
@@ -346,6 +349,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 
   // ---------------------------------------------------------------- state
   f32x4 acc[QT][DT];
+  // one key group: the row sums of P come from one more MFMA per chunk against
+  // an all-ones operand, complete in every lane (the same bf16 P as P V)
+  constexpr bool kMfmaSum = KG == 1;
+  f32x4 acc_l[QT];
+  bf16x8 ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16_t)1.0f;
   float m_run[QT], l_run[QT];
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
@@ -353,6 +363,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     l_run[i] = 0.0f;
 #pragma unroll
     for (int d = 0; d < DT; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_l[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   auto store_tile = [&](const bf16x8 (&kr)[K_UNITS], const bf16x8 (&vr)[VK], int stage) {
@@ -491,6 +502,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         const float alpha =
             (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
         l_run[i] *= alpha;
+        acc_l[i] *= alpha;
 #pragma unroll
         for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
         m_run[i] = m_new;
@@ -505,9 +517,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           for (int e = 0; e < 4; ++e) {
             const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
             pf[j][i][4 * st + e] = (bf16_t)pv;
-            psum += pv;
+            if constexpr (!kMfmaSum) psum += pv;
           }
-      l_run[i] += psum;
+      if constexpr (!kMfmaSum) l_run[i] += psum;
     }
 
     // O^T += V^T P^T over the tile: in chunk j this lane's 8 P values are the
@@ -522,6 +534,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + ((ck0 + 8 * lg) ^ sw));
 #pragma unroll
         for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[j][i], acc[i][d]);
+      }
+      if constexpr (kMfmaSum) {
+#pragma unroll
+        for (int i = 0; i < QT; ++i) acc_l[i] = mfma16x16x32(ones, pf[j][i], acc_l[i]);
       }
     }
   };
@@ -567,11 +583,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   }
 
   // ---------------------------------------------------------------- combine lanes
-  // the 4 lane groups of a query hold partial sums over their own keys
+  // the MFMA row sums are complete in every lane; the VALU ones are partial
+  // sums of the 4 lane groups of a query over their own keys
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
-    l_run[i] += partner_f32<4>(l_run[i]);
-    l_run[i] += partner_f32<5>(l_run[i]);
+    if constexpr (kMfmaSum) {
+      l_run[i] = acc_l[i][0];
+    } else {
+      l_run[i] += partner_f32<4>(l_run[i]);
+      l_run[i] += partner_f32<5>(l_run[i]);
+    }
   }
 
   // ---------------------------------------------------------------- combine key groups
