@@ -19,6 +19,11 @@ numbers.  Per case:
 - on the first call of each case every tree output, decision, path and drawn
   token equals the oracle's, sequences with a near-tie on either side excepted
   (they are counted and must stay rare).
+Two positions (V = 8): a root with 3 i.i.d. children, each with 2 i.i.d.
+children of its own, and rows that depend only on the token prefix.  The first
+emitted token follows p0 and, given first token x, the second follows p1[x]
+(chi-square per x, pooled), with the oracle's inputs and element-wise parity on
+the first call.
 """
 import sys
 
@@ -44,6 +49,11 @@ def log(*a):
 
 
 def _chi2_pvalue(counts, p):
+    stat, df = _chi2_stat(counts, p)
+    return stats.chi2.sf(stat, df)
+
+
+def _chi2_stat(counts, p):
     n = counts.sum()
     exp = n * p
     order = np.argsort(exp)
@@ -59,7 +69,7 @@ def _chi2_pvalue(counts, p):
         cb[-1] += acc_c
         eb[-1] += acc_e
     cb, eb = np.array(cb), np.array(eb)
-    return stats.chi2.sf(((cb - eb) ** 2 / eb).sum(), len(cb) - 1)
+    return ((cb - eb) ** 2 / eb).sum(), len(cb) - 1
 
 
 def _logits(seed, sigma):
@@ -143,3 +153,68 @@ def test_per_path_rejection_siblings_is_not_exact(gpu):
     pv = _chi2_pvalue(counts, softmax(lp.astype(np.float64)))
     log(f"  chi-square p-value {pv:.3g}")
     assert pv < 1e-3
+
+
+# ----------------------------------------------------------------------------
+# two positions
+# ----------------------------------------------------------------------------
+
+def _two_level_logits(seed, V=8, sigma=1.5):
+    rng = np.random.default_rng(seed)
+    lp0 = (3.0 * rng.standard_normal(V)).astype(np.float32)
+    lq0 = (lp0 + sigma * rng.standard_normal(V)).astype(np.float32)
+    lp1 = (3.0 * rng.standard_normal((V, V))).astype(np.float32)
+    lq1 = (lp1 + sigma * rng.standard_normal((V, V))).astype(np.float32)
+    return lp0, lq0, lp1, lq1
+
+
+def _two_emitted(token, acc_len, acc_path, next_token):
+    B = len(acc_len)
+    ar = np.arange(B)
+    x1 = np.where(acc_len >= 1, token[ar, np.maximum(acc_path[:, 1], 0)], next_token)
+    x2 = np.where(acc_len >= 2, token[ar, np.maximum(acc_path[:, 2], 0)], next_token)
+    return x1, np.where(acc_len >= 1, x2, -1)
+
+
+def test_two_level_sequential_follows_prefix_rows(gpu):
+    log(f"case sequential rejection over two positions, {TRIALS} trials at V=8")
+    logits = _two_level_logits(31)
+    lp0, _, lp1, _ = logits
+    V2 = len(lp0)
+    rng = np.random.default_rng(32)
+    x1s, x2s = [], []
+    for start in range(0, TRIALS, CHUNK):
+        B = min(CHUNK, TRIALS - start)
+        c = synth.make_two_level_trials(rng, B, *logits, 3, 2)
+        res = pipeline.Step(c, mode="reject_recursive", device="cuda:0", with_kv=False).run()
+        assert res["status"] == 0, res["status"]
+        x1, x2 = _two_emitted(res["token"], res["acc_len"], res["acc_path"], res["next_token"])
+        x1s.append(x1)
+        x2s.append(x2)
+        if start == 0:
+            tr = oracle.build_tree_explicit(c["cand_parent"], c["cand_token"], c["root_token"],
+                                            c["T_cap"])
+            for k in ("n_nodes", "parent", "token", "depth"):
+                assert np.array_equal(res[k], tr[k]), k
+            ora = oracle.verify("reject_recursive", c["tgt"], c["dft"], c["dft_row"],
+                                tr["n_nodes"], tr["parent"], tr["token"], tr["depth"],
+                                c["u_node"], c["u_final"])
+            ok = (res["near_tie"] == 0) & (ora["near_tie"] == 0)
+            log(f"  {int((~ok).sum())} of {B} sequences with a near-tie")
+            assert int((~ok).sum()) <= B // 1000
+            for k in ("acc_len", "acc_path", "next_token", "decision"):
+                assert np.array_equal(res[k][ok], ora[k][ok]), k
+    x1, x2 = np.concatenate(x1s), np.concatenate(x2s)
+    pv1 = _chi2_pvalue(np.bincount(x1, minlength=V2), softmax(lp0.astype(np.float64)))
+    stat, df = 0.0, 0
+    for x in range(V2):
+        sel = (x1 == x) & (x2 >= 0)
+        if sel.sum() < 50:
+            continue
+        s_, d_ = _chi2_stat(np.bincount(x2[sel], minlength=V2), softmax(lp1[x].astype(np.float64)))
+        stat += s_
+        df += d_
+    pv2 = stats.chi2.sf(stat, df)
+    log(f"  first token p-value {pv1:.4f}, second token given the first {pv2:.4f}, "
+        f"two tokens emitted in {(x2 >= 0).mean():.3f} of the trials")
+    assert pv1 >= 1e-3 and pv2 >= 1e-3

@@ -15,6 +15,11 @@
   (drafter-history page, DSpark acceptance label) within 4 sigma.
 - Special cases: q = p always accepts the first candidate; a one-hot p makes
   sequential rejection take the greedy path.
+- Two positions: with rows that depend only on the token prefix (a root whose
+  i.i.d. children each have their own i.i.d. children), the first emitted
+  token follows p0 and, given first token x, the second follows p1[x]; the
+  same trials with the depth-1 rows handed to the wrong siblings, and
+  per-path rejection, fail.
 """
 import numpy as np
 import pytest
@@ -193,6 +198,12 @@ def test_exact_path_marginal_is_target(oracle, seed, V, N, sigma):
 # ----------------------------------------------------------------------------
 
 def _chi2_pvalue(counts, p):
+    stat, df = _chi2_stat(counts, p)
+    return stats.chi2.sf(stat, df)
+
+
+def _chi2_stat(counts, p):
+    """Pearson statistic over bins merged (smallest first) to >= 5 expected, and its dof."""
     n = counts.sum()
     exp = n * p
     order = np.argsort(exp)
@@ -210,8 +221,7 @@ def _chi2_pvalue(counts, p):
         cb[-1] += acc_c
         eb[-1] += acc_e
     cb, eb = np.array(cb), np.array(eb)
-    chi2 = ((cb - eb) ** 2 / eb).sum()
-    return stats.chi2.sf(chi2, len(cb) - 1)
+    return ((cb - eb) ** 2 / eb).sum(), len(cb) - 1
 
 
 def _oracle_trials(oracle, mode, lp, lq, N, n_trials, seed, chunk=250_000):
@@ -369,3 +379,89 @@ def test_workload_inputs_run_through_oracle(oracle):
                             tr["parent"], tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
         assert 0 <= res["acc_len"][0] <= 4
         assert 0 <= res["next_token"][0] < inp["V"]
+
+
+# ----------------------------------------------------------------------------
+# two positions: the walk descends into the accepted child's own rows
+# ----------------------------------------------------------------------------
+
+def two_level_logits(seed, V=8, sigma=1.5):
+    rng = np.random.default_rng(seed)
+    lp0 = (3.0 * rng.standard_normal(V)).astype(np.float32)
+    lq0 = (lp0 + sigma * rng.standard_normal(V)).astype(np.float32)
+    lp1 = (3.0 * rng.standard_normal((V, V))).astype(np.float32)
+    lq1 = (lp1 + sigma * rng.standard_normal((V, V))).astype(np.float32)
+    return lp0, lq0, lp1, lq1
+
+
+def two_emitted(token, acc_len, acc_path, next_token):
+    """First and second emitted tokens of each trial (-1 where only one is emitted)."""
+    B = len(acc_len)
+    ar = np.arange(B)
+    x1 = np.where(acc_len >= 1, token[ar, np.maximum(acc_path[:, 1], 0)], next_token)
+    x2 = np.where(acc_len >= 2, token[ar, np.maximum(acc_path[:, 2], 0)], next_token)
+    return x1, np.where(acc_len >= 1, x2, -1)
+
+
+def two_level_pvalues(x1, x2, logits):
+    """p-values of x1 against p0 and of x2 given x1 = x against p1[x], pooled over x."""
+    lp0, _, lp1, _ = logits
+    V = len(lp0)
+    p0 = softmax(lp0.astype(np.float64))
+    pv1 = _chi2_pvalue(np.bincount(x1, minlength=V), p0)
+    stat, df = 0.0, 0
+    for x in range(V):
+        sel = (x1 == x) & (x2 >= 0)
+        if sel.sum() < 50:
+            continue
+        s_, d_ = _chi2_stat(np.bincount(x2[sel], minlength=V), softmax(lp1[x].astype(np.float64)))
+        stat += s_
+        df += d_
+    return pv1, stats.chi2.sf(stat, df)
+
+
+def rotate_depth1_rows(c, N1):
+    """Hand every depth-1 node the rows of the next sibling (a planted mistake)."""
+    c = dict(c)
+    c["tgt"] = c["tgt"].copy()
+    c["dft"] = c["dft"].copy()
+    c["tgt"][:, 1:1 + N1] = np.roll(c["tgt"][:, 1:1 + N1], -1, axis=1)
+    c["dft"][:, 1:1 + N1] = np.roll(c["dft"][:, 1:1 + N1], -1, axis=1)
+    return c
+
+
+def _oracle_two_level(oracle, mode, logits, n_trials, seed, N1=3, N2=2, plant=False,
+                      chunk=250_000):
+    rng = np.random.default_rng(seed)
+    x1s, x2s = [], []
+    for start in range(0, n_trials, chunk):
+        B = min(chunk, n_trials - start)
+        c = synth.make_two_level_trials(rng, B, *logits, N1, N2)
+        if plant:
+            c = rotate_depth1_rows(c, N1)
+        tr = oracle.build_tree_explicit(c["cand_parent"], c["cand_token"], c["root_token"],
+                                        c["T_cap"])
+        res = oracle.verify(mode, c["tgt"], c["dft"], c["dft_row"], tr["n_nodes"], tr["parent"],
+                            tr["token"], tr["depth"], c["u_node"], c["u_final"])
+        x1, x2 = two_emitted(tr["token"], res["acc_len"], res["acc_path"], res["next_token"])
+        x1s.append(x1)
+        x2s.append(x2)
+    return np.concatenate(x1s), np.concatenate(x2s)
+
+
+def test_two_level_sequential_follows_prefix_rows(oracle):
+    logits = two_level_logits(31)
+    x1, x2 = _oracle_two_level(oracle, "reject_recursive", logits, 1_000_000, seed=32)
+    pv1, pv2 = two_level_pvalues(x1, x2, logits)
+    assert pv1 >= 1e-3 and pv2 >= 1e-3, (pv1, pv2)
+    # both depths are exercised: many trials emit two tokens through a depth-2 acceptance
+    assert (x2 >= 0).mean() > 0.5
+
+
+def test_two_level_negative_controls(oracle):
+    logits = two_level_logits(31)
+    x1, x2 = _oracle_two_level(oracle, "reject_recursive", logits, 1_000_000, seed=33,
+                               plant=True)
+    assert two_level_pvalues(x1, x2, logits)[1] < 1e-3
+    x1, x2 = _oracle_two_level(oracle, "reject_path", logits, 1_000_000, seed=34)
+    assert two_level_pvalues(x1, x2, logits)[0] < 1e-3

@@ -271,3 +271,46 @@ def make_custom_inputs(seed: int, *, B: int, H: int, Hkv: int, D: int, V: int, d
     out["k"] = conv(_normal(rngs["k"], (B, Hkv, cap, D)))
     out["v"] = conv(_normal(rngs["v"], (B, Hkv, cap, D)))
     return out
+
+
+def make_two_level_trials(rng: np.random.Generator, B: int, lp0: np.ndarray, lq0: np.ndarray,
+                          lp1: np.ndarray, lq1: np.ndarray, N1: int, N2: int) -> dict:
+    """B independent two-position trials whose rows depend only on the token prefix.
+
+    A root with N1 children drawn i.i.d. from softmax(lq0), each child with
+    token x having N2 children drawn i.i.d. from softmax(lq1[x]); the target row
+    of the root is lp0 and of a depth-1 node with token x is lp1[x] (as a model's
+    rows depend on the prefix only), and the draft rows match.  Depth-2 nodes are
+    leaves (target row lp0, unused by the first two emitted tokens).  Node
+    numbering: depth-1 candidate i is node 1 + i, its j-th child node
+    1 + N1 + i*N2 + j.
+    """
+    V = len(lp0)
+    N = N1 + N1 * N2
+    T_cap = 1 + N
+    cand_parent = np.zeros((B, N), np.int32)
+    cand_token = np.zeros((B, N), np.int32)
+    tok1 = _inverse_cdf_draws(lq0, rng.random((B, N1)).ravel()).reshape(B, N1)
+    cand_token[:, :N1] = tok1
+    u2 = rng.random((B, N1, N2))
+    for x in range(V):
+        sel = tok1 == x
+        if sel.any():
+            draws = _inverse_cdf_draws(lq1[x], u2[sel].ravel()).reshape(-1, N2)
+            idx_b, idx_i = np.nonzero(sel)
+            for j in range(N2):
+                cand_token[idx_b, N1 + idx_i * N2 + j] = draws[:, j]
+    for i in range(N1):
+        cand_parent[:, N1 + i * N2:N1 + (i + 1) * N2] = 1 + i
+    tgt = np.empty((B, T_cap, V), np.float32)
+    tgt[:] = lp0
+    tgt[:, 1:1 + N1] = lp1[tok1]
+    dft = np.empty((B, 1 + N1, V), np.float32)
+    dft[:, 0] = lq0
+    dft[:, 1:] = lq1[tok1]
+    dft_row = np.full((B, T_cap), -1, np.int32)
+    dft_row[:, :1 + N1] = np.arange(1 + N1, dtype=np.int32)
+    return dict(B=B, T_cap=T_cap, V=V, tree="explicit", cand_parent=cand_parent,
+                cand_token=cand_token, root_token=np.zeros(B, np.int32), tgt=tgt, dft=dft,
+                dft_row=dft_row, u_node=exact_uniforms(rng, (B, T_cap)),
+                u_final=exact_uniforms(rng, (B,)))
