@@ -33,6 +33,7 @@ sys.path.insert(0, str(ROOT))
 
 METRIC = "verified tree tokens/s per verify step; attention+verify HBM GB/s as % of peak"
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # dense
 MALL_BYTES = 256 << 20
 
 
@@ -93,6 +94,17 @@ def attention_bytes(inp, n_nodes):
         total += 2 * Hkv * keys * D * esz          # K and V
         total += 2 * T * H * D * esz               # q in, out
         total += T * n_words * 8                   # masks
+    return total
+
+
+def attention_flops(inp, n_nodes):
+    """Algorithmic flops of one spec_tree_attention launch: Q K^T and P V over
+    the context and the tree for every live (node, head) row, 2 flops per MAC."""
+    D, H = inp["D"], inp["H"]
+    total = 0
+    for b in range(inp["B"]):
+        T = int(n_nodes[b])
+        total += 4 * H * T * (int(inp["ctx_len"][b]) + T) * D
     return total
 
 
@@ -249,10 +261,11 @@ def main():
     brk = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) * 1e3 for n in names}
 
     # algorithmic bytes (averaged over the rotation)
-    a_bytes, v_bytes = [], []
+    a_bytes, v_bytes, a_flops = [], [], []
     for inp, st in steps_all:
         nn = st.n_nodes.cpu().numpy()
         a_bytes.append(attention_bytes(inp, nn))
+        a_flops.append(attention_flops(inp, nn))
         v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
                                     inp["dft_row"] if inp["dft_row"] is not None else None, mode,
                                     st.decision.cpu().numpy()))
@@ -260,6 +273,18 @@ def main():
     a_avg = float(np.mean([a_bytes[i % n_sets] for i in sorted(ev)]))
     v_avg = float(np.mean(v_bytes))
     achieved = a_avg / attn_avg_s / 1e9
+    f_avg = float(np.mean([a_flops[i % n_sets] for i in sorted(ev)]))
+    # the bound the call's arithmetic intensity puts it under (bf16 MFMA peak
+    # over HBM peak is the ridge); the fp32 path is always reported against HBM
+    ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    mfma_bound = wl.dtype == "bf16" and f_avg / a_avg > ridge
+    if mfma_bound:
+        tflops = f_avg / attn_avg_s / 1e12
+        roof = {"bound": "mfma", "achieved": tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": tflops / BF16_MFMA_PEAK_TFLOPS}
+    else:
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS}
     status = max(int(st.status.item()) for _, st in steps_all)
 
     line = {
@@ -278,8 +303,9 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "ctx": wl.ctx, "H": wl.H, "Hkv": wl.Hkv,
                    "D": wl.D, "V": wl.V, "tree": wl.tree, "mode": mode, "T_cap": wl.T_cap,
                    "draft_nodes_per_step": float(np.mean(n_draft)), "input_sets": n_sets},
-        "roofline": {"bound": "hbm", "kernel": "spec_tree_attention", "achieved": achieved,
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+        "roofline": {**roof, "kernel": "spec_tree_attention",
+                     "arithmetic_intensity": f_avg / a_avg, "algorithmic_flops_per_launch": f_avg,
+                     "hbm_GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counted_traffic(wl.name), "algorithmic_bytes_per_launch": a_avg,
                      "avg_launch_us": attn_avg_s * 1e6, "timed_launches": len(ev)},
         "copy_probe": {"bytes": 2 * n_probe, "GBps": probe_gbps,

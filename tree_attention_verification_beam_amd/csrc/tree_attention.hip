@@ -773,27 +773,53 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
   const uint64_t* arow = anc + ((size_t)b * T_cap + t) * n_words;
   const float* kb = kc + ((size_t)b * Hkv + g) * cache_cap * D;
   const float* vb = vc + ((size_t)b * Hkv + g) * cache_cap * D;
+  const int n_keys = ctx + T;
   float m = -INFINITY, l = 0.0f;
-  for (int j = 0; j < ctx + T; ++j) {
-    if (j >= ctx) {
-      const int aa = j - ctx;
-      if (!((arow[aa >> 6] >> (aa & 63)) & 1ull)) continue;
-    }
-    float part = 0.0f;
+  // keys in chunks of KC: every K and V load of a chunk is issued before any
+  // is used, so a chunk costs one memory round trip
+  constexpr int KC = 16;
+  for (int j0 = 0; j0 < n_keys; j0 += KC) {
+    float kv[KC][MAXD], vv[KC][MAXD];
+    bool vis[KC];
 #pragma unroll
-    for (int jj = 0; jj < MAXD; ++jj) {
-      const int d = lane + 64 * jj;
-      if (d < D) part += qv[jj] * kb[(size_t)j * D + d];
+    for (int c = 0; c < KC; ++c) {
+      const int j = j0 + c;
+      bool v = j < n_keys;
+      if (v && j >= ctx) {
+        const int aa = j - ctx;
+        v = (arow[aa >> 6] >> (aa & 63)) & 1ull;
+      }
+      vis[c] = v;
+#pragma unroll
+      for (int jj = 0; jj < MAXD; ++jj) {
+        const int d = lane + 64 * jj;
+        const bool in = j < n_keys && d < D;
+        kv[c][jj] = in ? kb[(size_t)j * D + d] : 0.0f;
+        vv[c][jj] = in ? vb[(size_t)j * D + d] : 0.0f;
+      }
     }
-    const float s = wave_sum_f32(part) * scale;
-    const float m_new = fmaxf(m, s);
+    float sc[KC];
+    float cmax = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      float part = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < MAXD; ++jj) part += qv[jj] * kv[c][jj];
+      sc[c] = wave_sum_f32(part) * scale;
+      if (vis[c]) cmax = fmaxf(cmax, sc[c]);
+    }
+    if (cmax == -INFINITY) continue;  // no visible key in the chunk (uniform)
+    const float m_new = fmaxf(m, cmax);
     const float alpha = __expf(m - m_new);
-    const float p = __expf(s - m_new);
-    l = l * alpha + p;
+    l *= alpha;
 #pragma unroll
-    for (int jj = 0; jj < MAXD; ++jj) {
-      const int d = lane + 64 * jj;
-      if (d < D) acc[jj] = acc[jj] * alpha + p * vb[(size_t)j * D + d];
+    for (int jj = 0; jj < MAXD; ++jj) acc[jj] *= alpha;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      const float p = vis[c] ? __expf(sc[c] - m_new) : 0.0f;
+      l += p;
+#pragma unroll
+      for (int jj = 0; jj < MAXD; ++jj) acc[jj] += p * vv[c][jj];
     }
     m = m_new;
   }
