@@ -85,8 +85,9 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
     p.KG = 1; p.QT = 2; p.PF = 2;
   } else {
     // many rows (wide GQA groups): 128-row blocks of 4 waves with two query
-    // tiles each read the same key range, two workgroups per CU
-    p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 1;
+    // tiles each read the same key range, two workgroups per CU, two tiles of
+    // loads in flight
+    p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 2;
   }
   const long units = (long)B * Hkv;
   const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
@@ -860,6 +861,7 @@ int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   SPEC_ATTN_CASE(8, 1, 2, 2)
   SPEC_ATTN_CASE(8, 1, 1, 2)
   SPEC_ATTN_CASE(8, 2, 1, 2)
+  SPEC_ATTN_CASE(4, 2, 1, 2)
 #undef SPEC_ATTN_CASE
   return SPEC_ERR_UNSUPPORTED;
 }
