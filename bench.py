@@ -144,7 +144,7 @@ def verify_bytes(inp, n_nodes, parent, dft_row, mode, decision=None):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
