@@ -1,0 +1,85 @@
+"""Consecutive verification steps on one cache, against the oracle at every step.
+
+ReDrafter page, "The Full Speculative Decoding Loop", Steps 4-6: the target
+attends over its cache plus the packed tree, a prefix is accepted, and the
+accepted path's K/V become part of the context for the next step.  Here three
+steps run back to back on one GPU cache (bf16, 8 query heads over 2 KV heads,
+D = 128, two sequences with different context lengths): each step writes the
+new tree's K/V after the context grown by the step before, builds the tree,
+attends, verifies greedily (with planted matches so paths are accepted) and
+commits.  The oracle runs the same steps on a host copy of the cache.  Every
+step must give the same trees, verify outputs, context lengths and cache
+contents (bit-exact) and attention within 1e-2 of the largest output.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tree_attention_verification_beam_amd import pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def log(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _to_numpy_bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_three_steps_share_one_cache(gpu):
+    B, H, Hkv, D, V, W, L = 2, 8, 2, 128, 2000, 4, 4
+    T_cap = 1 + W * L
+    ctx = np.array([300, 457], np.int32)
+    n_steps = 3
+    cap = int(ctx.max()) + n_steps * (L + 1) + T_cap
+    rng = np.random.default_rng(77)
+    k_host = synth.f32_to_bf16_bits(rng.standard_normal((B, Hkv, cap, D), dtype=np.float32))
+    v_host = synth.f32_to_bf16_bits(rng.standard_normal((B, Hkv, cap, D), dtype=np.float32))
+    total_acc = 0
+    for s in range(n_steps):
+        inp = synth.make_custom_inputs(500 + s, B=B, H=H, Hkv=Hkv, D=D, V=V, dtype="bf16",
+                                       ctx_lens=ctx, tree="beams", W=W, L=L)
+        # this step's tree K/V go right after each sequence's context
+        for b in range(B):
+            c = int(ctx[b])
+            k_host[b, :, c:c + T_cap] = inp["k"][b, :, c:c + T_cap]
+            v_host[b, :, c:c + T_cap] = inp["v"][b, :, c:c + T_cap]
+        inp["k"], inp["v"] = k_host.copy(), v_host.copy()
+        inp["cap"] = cap
+        tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], T_cap)
+        # plant a matching prefix in one beam of each sequence
+        tgt = inp["tgt"].copy()
+        for b in range(B):
+            i = int(rng.integers(0, W))
+            a = int(rng.integers(1, L + 1))
+            for d in range(a):
+                par = 0 if d == 0 else tr["beam_node"][b, i, d - 1]
+                tgt[b, par, inp["beams"][b, i, d]] = tgt[b, par].max() + 20.0
+        inp["tgt"] = tgt
+        log(f"case step {s}: ctx {ctx.tolist()}")
+        step = pipeline.Step(inp, "greedy")
+        res = step.run(compact=True)
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        for key in ("n_nodes", "parent", "token", "depth", "anc"):
+            assert np.array_equal(res[key], tr[key]), (s, key)
+        att = oracle.tree_attention(inp["q"], k_host, v_host, ctx, tr["n_nodes"], tr["anc"])
+        err = np.abs(res["attn"].astype(np.float64) - att).max()
+        assert err <= 1e-2 * np.abs(att).max(), (s, err)
+        ver = oracle.verify("greedy", tgt, None, None, tr["n_nodes"], tr["parent"], tr["token"],
+                            tr["depth"], inp["u_node"], inp["u_final"])
+        for key in ("acc_len", "acc_path", "next_token", "decision"):
+            assert np.array_equal(res[key], ver[key]), (s, key)
+        # the commit, on the oracle's copy of the same cache
+        new_ctx = oracle.kv_compact(k_host, v_host, ctx, ver["acc_len"], ver["acc_path"])
+        assert np.array_equal(res["ctx_len"], new_ctx), s
+        assert np.array_equal(_to_numpy_bits(step.k), k_host), s
+        assert np.array_equal(_to_numpy_bits(step.v), v_host), s
+        total_acc += int(ver["acc_len"].sum())
+        ctx = new_ctx
+    assert total_acc >= n_steps  # the planted matches were accepted
