@@ -1,0 +1,42 @@
+"""Tree attention across the context-split counts the plan can choose.
+
+The context of a (sequence, KV head) is split over workgroups so that the grid
+covers the CUs; a merge kernel then combines the (max, sum, O) partials.  The
+shapes below make the plan choose 1, 2, 4, 21 and 32 splits (the last two with
+two and with one key group), each compared with the oracle within 1e-2 of the
+largest output, with ragged contexts where B > 1.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tree_attention_verification_beam_amd import pipeline, synth
+
+from test_gpu_parity import attn_bar, log
+
+pytestmark = pytest.mark.gpu
+
+# (B, H, Hkv, context lengths): splits chosen by the plan for 4 beams of 4
+CASES = {
+    "1 split": (1, 2, 2, [150]),
+    "2 splits": (4, 16, 16, [300, 41, 299, 0]),
+    "4 splits": (2, 32, 32, [1000, 777]),
+    "21 splits": (1, 1, 1, [4000]),
+    "32 splits, GQA": (1, 4, 1, [8000]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_attention_split_counts(gpu, case):
+    B, H, Hkv, ctx = CASES[case]
+    inp = synth.make_custom_inputs(9100 + len(case), B=B, H=H, Hkv=Hkv, D=128, V=500,
+                                   dtype="bf16", ctx_lens=ctx, tree="beams", W=4, L=4)
+    log(f"case {case}: B={B} H={H} Hkv={Hkv} ctx={ctx}")
+    tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+    res = pipeline.Step(inp, "greedy").run(compact=False)
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    attn_bar(res["attn"], ref, case)
+    for b in range(B):
+        assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)
