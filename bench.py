@@ -465,8 +465,17 @@ def cpu_baseline(inp, mode, budget_s):
         draft += int(tr["n_nodes"].sum()) - inp["B"]
         if t_total > 0.5 * budget_s:
             break
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": draft / t_total, "unit": "verified tree tokens/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": cpu, "host_visible_cores": os.cpu_count(),
             "sample": f"{done} full step(s) of workload {inp['name']} (build, attention over all "
                       f"rows, {mode} verify, compact), fp64 single-threaded C; "
                       f"{t_total:.1f} s on {os.cpu_count()} visible host cores"}
