@@ -29,6 +29,15 @@
  *     for the bonus token after t); dft_row[t] names the draft row the children
  *     of t were drawn from.
  *   - Padding: parent/token/depth = -1 and an all-zero mask for t >= T.
+ *
+ * Pins: every function is checked in the test suite against values the pages
+ * print, closed forms, brute force or a second formulation, with one
+ * exception.  PARITY UNPINNED: the tree-level output distribution of per-path
+ * rejection (mode 1) when a node has two or more children.  That mode is not
+ * distribution-exact then (only sequential checking is), so no target
+ * distribution exists to test it against; only its agreement with an
+ * independent per-beam formulation, and its single-child case (plain
+ * speculative sampling, chi-square), are pinned.
  */
 #include <math.h>
 #include <stdint.h>
