@@ -1,25 +1,27 @@
 """Benchmark of one speculative verification step on one MI355X.
 
 A step is the whole hot path over one batch of synthetic input: spec_build_tree,
-spec_tree_attention, spec_verify and spec_kv_compact, enqueued on one stream,
-preceded by restoring the sequence's context length (the commit advances it)
-with the library's copy kernel.  The calls are marshalled once (prepared), so
-the host issues a step faster than the GPU runs it.
-Inputs already sit in HBM.  To keep the measurement honest about HBM (the
-256 MB Infinity Cache would otherwise hold a small workload), the timed steps
-rotate over several independent input sets whose total exceeds twice the
-cache, so each step reads data that was evicted since its last use.
+spec_tree_attention, spec_verify and spec_kv_compact, enqueued on one stream.
+The calls are marshalled once (prepared), so the host issues a step faster than
+the GPU runs it.  Inputs already sit in HBM.  To keep the measurement honest
+about HBM (the 256 MB Infinity Cache would otherwise hold a small workload), the
+timed steps rotate over several independent input sets whose total exceeds
+twice the cache, so each step reads data that was evicted since its last use.
+
+The default workload is the 64-sequence static-tree step (B=64, ctx 1024,
+32/32 heads of 128, vocabulary 128000): the largest per-step working set of the
+five configurations (1.1 GB of K/V, 0.56 GB of logits), bound by HBM.
 
 Prints one JSON line: verified tree tokens/s (draft nodes checked per second),
-the roofline of the dominant kernel measured with HIP events on the launch
-stream, and the CPU oracle timed on the host as a baseline.
+the roofline of the dominant kernel (the attention call, each call's average
+launch duration from HIP events around a batch of back-to-back launches on the
+launch stream), and the CPU oracle timed on the host as a baseline.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -42,15 +44,15 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive | greedy_walk")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
     ap.add_argument("--probe-mib", type=int, default=512,
                     help="size of the plain copy that calibrates bandwidth and counters")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="time the attention call with HIP events on every n-th timed step")
+    ap.add_argument("--roof-launches", type=int, default=32,
+                    help="back-to-back launches per call in the per-call timing (>= 20)")
     return ap.parse_args()
 
 
@@ -210,31 +212,17 @@ def main():
     # ---------------------------------------------------------------- timed steps
     # every step starts from the set's initial context: step i uses its own
     # copy of the context lengths (staged here), so no restore runs in the
-    # timed region.  The attention call of every n-th step is bracketed by HIP
-    # events on the launch stream: a timing event costs a few microseconds of
-    # GPU time here, so events around every call would slow the very steps
-    # they time.
+    # timed region, and nothing but the four calls is enqueued there.
     uses = -(-args.steps // n_sets)
     for _, st in steps_all:
         st.prepare_fresh_contexts(uses, stream)
-    every = max(1, args.event_every)
-    while math.gcd(every, n_sets) != 1:  # sample every input set
-        every += 1
-    timed = set(range(0, args.steps, every))
-    ev = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for i in timed}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         inp, st = steps_all[i % n_sets]
         k = i // n_sets
         st.p_build()
-        if i in ev:
-            ev[i][0].record(stream)
-            st.p_attention_fresh[k]()
-            ev[i][1].record(stream)
-        else:
-            st.p_attention_fresh[k]()
+        st.p_attention_fresh[k]()
         st.p_verify()
         st.p_compact_fresh[k]()
     torch.cuda.synchronize()
@@ -242,38 +230,59 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     verified = sum(n_draft[i % n_sets] for i in range(args.steps))
     value = verified / (t1 - t0)
-    attn_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in sorted(ev)]
-    attn_avg_s = float(np.mean(attn_ms)) * 1e-3
 
-    # ---------------------------------------------------------------- per-call breakdown
-    names = ("build", "attention", "verify", "compact")
-    evs = {n: [] for n in names}
-    for i in range(min(args.steps, 4 * n_sets)):
-        inp, st = steps_all[i % n_sets]
-        st.p_reset()
-        for n, fn in zip(names, (st.p_build, st.p_attention, st.p_verify, st.p_compact)):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            evs[n].append((a, b))
-    torch.cuda.synchronize()
-    brk = {n: float(np.mean([a.elapsed_time(b) for a, b in evs[n]])) * 1e3 for n in names}
+    # ---------------------------------------------------------------- per-call timing
+    # each call alone, launched n times back to back over the rotation of
+    # input sets (cold data as in the steps) between one pair of HIP events on
+    # the launch stream, so the events' own cost is spread over the batch; the
+    # average launch duration of the attention call is the roofline's.
+    n_roof = max(20, args.roof_launches, 2 * n_sets)
+
+    def batch_us(calls, warm=True):
+        if warm:
+            for c in calls[:2]:
+                c()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for c in calls:
+            c()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / len(calls)
+
+    for _, st in steps_all:
+        st.p_reset()       # the commit advanced ctx_len: restore it
+    rot = [steps_all[i % n_sets][1] for i in range(n_roof)]
+    brk = {"build": batch_us([st.p_build for st in rot]),
+           "attention": batch_us([st.p_attention for st in rot]),
+           "verify": batch_us([st.p_verify for st in rot])}
+    one_pass = None
+    if mode == "greedy_walk":
+        # the one-pass greedy verify on the same trees and rows: every target row
+        # read once and every node tested (the walk reads only surviving nodes' rows)
+        calls = [st.prepare_verify_mode("greedy", stream) for _, st in steps_all]
+        one_pass = batch_us([calls[i % n_sets] for i in range(n_roof)])
+        brk["verify_one_pass_greedy"] = one_pass
+    # (each commit on a fresh copy of the context lengths, used once: the call
+    # is warm from the steps already)
+    uses_c = -(-n_roof // n_sets)
+    for _, st in steps_all:
+        st.prepare_fresh_contexts(uses_c, stream)
+    brk["compact"] = batch_us([steps_all[i % n_sets][1].p_compact_fresh[i // n_sets]
+                               for i in range(n_roof)], warm=False)
+    attn_avg_s = brk["attention"] * 1e-6
 
     # warm figure, labelled as such: one input set's attention call back to
     # back, so a workload that fits the Infinity Cache reads it from there
     inp0, st0 = steps_all[0]
     st0.p_reset()
-    for _ in range(5):
-        st0.p_attention()
-    wa, wb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n_warm = 50
-    wa.record(stream)
-    for _ in range(n_warm):
-        st0.p_attention()
-    wb.record(stream)
+    warm_us = batch_us([st0.p_attention] * 50)
+
+    # the walk's bytes follow its own decisions: run it again on every set (the
+    # one-pass call above shares its outputs)
+    for _, st in steps_all:
+        st.p_verify()
     torch.cuda.synchronize()
-    warm_us = wa.elapsed_time(wb) * 1e3 / n_warm
 
     # algorithmic bytes (averaged over the rotation)
     a_bytes, v_bytes, a_flops = [], [], []
@@ -284,11 +293,13 @@ def main():
         v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
                                     inp["dft_row"] if inp["dft_row"] is not None else None, mode,
                                     st.decision.cpu().numpy()))
+    v1_bytes = [verify_bytes(inp, st.n_nodes.cpu().numpy(), None, None, "greedy")
+                for inp, st in steps_all]
     n_accept = [int(st.acc_len.sum().item()) + st.B for _, st in steps_all]
-    a_avg = float(np.mean([a_bytes[i % n_sets] for i in sorted(ev)]))
-    v_avg = float(np.mean(v_bytes))
+    a_avg = float(np.mean([a_bytes[i % n_sets] for i in range(n_roof)]))
+    v_avg = float(np.mean([v_bytes[i % n_sets] for i in range(n_roof)]))
     achieved = a_avg / attn_avg_s / 1e9
-    f_avg = float(np.mean([a_flops[i % n_sets] for i in sorted(ev)]))
+    f_avg = float(np.mean([a_flops[i % n_sets] for i in range(n_roof)]))
     # the bound the call's arithmetic intensity puts it under (bf16 MFMA peak
     # over HBM peak is the ridge); the fp32 path is always reported against HBM
     ridge = BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
@@ -322,7 +333,7 @@ def main():
                      "arithmetic_intensity": f_avg / a_avg, "algorithmic_flops_per_launch": f_avg,
                      "hbm_GBps": achieved, "hbm_frac": achieved / HBM_PEAK_GBPS,
                      "traffic": counted_traffic(wl.name), "algorithmic_bytes_per_launch": a_avg,
-                     "avg_launch_us": attn_avg_s * 1e6, "timed_launches": len(ev)},
+                     "avg_launch_us": attn_avg_s * 1e6, "timed_launches": n_roof},
         "attention_warm": {"avg_call_us": warm_us, "input_set": 0,
                            "note": "one input set back to back: cache-resident where it fits"},
         "copy_probe": {"bytes": 2 * n_probe, "GBps": probe_gbps,
@@ -337,6 +348,12 @@ def main():
                 / HBM_PEAK_GBPS,
         },
         "device_status": status,
+        **({"verify_one_pass_greedy": {
+            "avg_call_us": one_pass, "bytes_per_launch": float(np.mean(v1_bytes)),
+            "GBps": float(np.mean(v1_bytes)) / (one_pass * 1e-6) / 1e9,
+            "note": "one-pass greedy verify on the same trees: every target row read, every "
+                    "node tested; the step uses the greedy walk, same accepted path"}}
+           if one_pass is not None else {}),
         # beside `value`: verified nodes per second of attention + verify time
         # only, and accepted tokens (acc_len + 1 per sequence) per step time
         "verified_tokens_per_s_attention_verify":

@@ -179,9 +179,7 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  *                         depth by depth, each such node's row is scanned and
  *                         its children are tested.  Only tested nodes (children
  *                         of such nodes) get decision and p_tok; the others get
- *                         -1 and 0.  Its workspace must be zero-filled before
- *                         its first call; every call leaves it ready for the
- *                         next (its counters back at zero).
+ *                         -1 and 0.
  * Draws are inverse-CDF in ascending vocabulary order: the smallest v whose
  * running sum exceeds u_final * total.
  *
@@ -204,9 +202,14 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * at each call) launches such grids cooperatively instead (guaranteed
  * residency, some 17 us slower per call).  A meeting that cannot complete ends at its wait bound and raises
  * SPEC_DEV_SYNC_TIMEOUT.
- * ws: spec_verify_workspace_size() bytes (no initial contents needed, except in
- * SPEC_GREEDY_WALK: zero-filled before the first call, see above).  Calls
- * that overlap in time must not share a workspace.
+ * A call that raised SPEC_DEV_SYNC_TIMEOUT has undefined acceptance outputs;
+ * its workspace stays usable (every call tags its exchange words with a new
+ * epoch, so words left by late workgroups of an earlier call never match).
+ * ws: spec_verify_workspace_size() bytes, no initial contents needed.  Calls
+ * that overlap in time must not share a workspace.  The workspace size is 0
+ * (and the call returns SPEC_ERR_UNSUPPORTED) for a vocabulary beyond what
+ * the row merge stages: more than 1024 chunks of 8192 entries (V > 8388608)
+ * in the one-pass modes, V * 4 >= 2^31 in SPEC_GREEDY_WALK.
  */
 size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R);
 int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, const float *dft,
@@ -227,16 +230,21 @@ int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, cons
  * root and the accepted tokens; next_token is the next step's root).
  * dt selects the element size; k_cache, v_cache [B][Hkv][cache_cap][D] in
  * place; ctx_len [B] in/out, each in [0, cache_cap); acc_len [B], acc_path
- * [B][T_cap] from spec_verify.  Requires cache_cap < 2^24 and Hkv <= 63
- * (SPEC_ERR_UNSUPPORTED otherwise): while the call runs, ctx_len[b] also
- * counts the arriving workgroups in its top bits, so nothing else may read it
- * until the call has finished on `stream`.
+ * [B][T_cap] from spec_verify.  One path's rows of one KV head must fit 64 KiB
+ * ((T_cap - 1) * D * element size <= 65536; SPEC_ERR_UNSUPPORTED otherwise).
+ * ctx_len[b] holds nothing but the length at any time: it is read, then
+ * written once after every read of it.
+ * ws: spec_kv_compact_workspace_size(B) bytes (per sequence an arrival
+ * counter of the call's workgroups), zero-filled before its first use; every
+ * call returns it to zero.  Calls that overlap in time must not share it.
  * A path that is not increasing or leaves the cache raises SPEC_DEV_CTX_RANGE
  * and that sequence is left untouched.
  */
+size_t spec_kv_compact_workspace_size(int B);
 int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int T_cap, void *k_cache,
                     void *v_cache, int32_t *ctx_len, const int32_t *acc_len,
-                    const int32_t *acc_path, int32_t *status, void *stream);
+                    const int32_t *acc_path, void *ws, size_t ws_bytes, int32_t *status,
+                    void *stream);
 
 /*
  * spec_beam_topk -- the pruning step of beam search, feeding spec_build_tree.
@@ -291,6 +299,21 @@ int spec_select_tree(int B, int N, int N_keep, const int32_t *cand_parent,
                      const int32_t *cand_token, const float *cand_logp, int32_t *keep_parent,
                      int32_t *keep_token, int32_t *keep_src, float *keep_score, int32_t *status,
                      void *stream);
+
+/*
+ * spec_last_device_status -- the SPEC_DEV_* bits a status word holds, read on
+ * the host once `stream` has finished.
+ *
+ * The calls are asynchronous, so problems seen by their kernels cannot be
+ * returned by the call (general contract above).  status_dev: a caller's
+ * device status word, as passed to the calls, or NULL for the library's own
+ * word on the current device, which every call that is passed no status word
+ * uses instead.  Synchronises `stream` (hipStream_t; NULL = default stream)
+ * and returns the word's bits (>= 0), or SPEC_ERR_HIP if the runtime fails.
+ * The library's own word is cleared after it is read; a caller's word is left
+ * as it is.  Not for use inside stream capture (it synchronises).
+ */
+int spec_last_device_status(const int32_t *status_dev, void *stream);
 
 /*
  * spec_copy_probe -- plain streaming copy of n_bytes (multiple of 16) from src

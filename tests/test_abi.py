@@ -34,7 +34,7 @@ def lib():
 def test_header_lists_the_calls():
     d = declared()
     for name in ("spec_build_tree", "spec_tree_attention", "spec_verify", "spec_kv_compact",
-                 "spec_beam_topk", "spec_select_tree"):
+                 "spec_beam_topk", "spec_select_tree", "spec_last_device_status"):
         assert name in d
 
 
@@ -91,7 +91,7 @@ def test_validation_rejects_before_launch(lib):
     assert cdll.spec_verify(7, 1, 17, 100, 0, *([1] * 17), 0, None, None) == -1
     assert cdll.spec_tree_attention(1, 1, 17, 6, 4, 128, 100, 64, *([1] * 6), 0.0, 1, None, 0,
                                     None, None) == -1
-    assert cdll.spec_kv_compact(1, 1, 8, 128, 10, 200, *([1] * 5), None, None) == -3
+    assert cdll.spec_kv_compact(1, 1, 8, 128, 10, 200, *([1] * 5), 16, 256, None, None) == -3
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -102,7 +102,8 @@ def test_empty_batch_is_a_no_op(lib):
     assert cdll.spec_tree_attention(1, 0, 17, 32, 32, 128, 1100, 1024, *([None] * 6), 0.0, None,
                                     None, 0, None, None) == 0
     assert cdll.spec_verify(0, 0, 17, 1000, 0, *([None] * 17), 0, None, None) == 0
-    assert cdll.spec_kv_compact(1, 0, 8, 128, 1100, 17, *([None] * 5), None, None) == 0
+    assert cdll.spec_kv_compact(1, 0, 8, 128, 1100, 17, *([None] * 5), None, 0, None,
+                                None) == 0
 
 
 def test_attention_rejects_a_row_block_beyond_32_bit_ranges(lib):
@@ -112,3 +113,30 @@ def test_attention_rejects_a_row_block_beyond_32_bit_ranges(lib):
     cap = (1 << 23) + 1  # * 128 * 2 bytes > 2^31
     assert cdll.spec_tree_attention(1, 1, 17, 32, 32, 128, cap, 1024, *([16] * 6), 0.0, 16,
                                     None, 0, None, None) == -2
+
+
+def test_verify_refuses_a_vocabulary_beyond_the_row_merge(lib):
+    """The one-pass verify merges a row's chunk partials in LDS batches of 1024
+    chunks of at most 8192 entries: a larger vocabulary is refused on the host
+    (workspace size 0, SPEC_ERR_UNSUPPORTED) before anything is launched."""
+    cdll = lib.load()
+    big = 32 * 256 * 1024 + 1
+    assert cdll.spec_verify_workspace_size(0, 1, 17, 32 * 256 * 1024, 0) > 0
+    for mode in (0, 1, 2):
+        assert cdll.spec_verify_workspace_size(mode, 1, 17, big, 4) == 0
+        assert cdll.spec_verify(mode, 1, 17, big, 4, *([16] * 17), 1 << 30, None, None) == -2
+    # the walk addresses a row through a 32-bit byte range
+    assert cdll.spec_verify(3, 1, 17, 1 << 29, 0, *([16] * 17), 1 << 30, None, None) == -2
+
+
+def test_compact_refuses_a_path_beyond_its_buffer(lib):
+    """One path's rows of one KV head go through a 64 KiB LDS buffer:
+    (T_cap - 1) rows of D values must fit it.  fp32 rows of 128 values at
+    T_cap 128 (63.5 KiB) pass the check, 256 values are refused; a missing or
+    small workspace is refused too."""
+    cdll = lib.load()
+    ptrs = [16] * 5
+    assert cdll.spec_kv_compact(0, 1, 8, 256, 10000, 128, *ptrs, 256, 256, None, None) == -2
+    assert cdll.spec_kv_compact(0, 1, 8, 128, 10000, 128, *ptrs, None, 0, None, None) == -4
+    assert cdll.spec_kv_compact(0, 300, 8, 128, 10000, 128, *ptrs, 256, 256, None, None) == -4
+    assert cdll.spec_kv_compact_workspace_size(300) == 1280

@@ -91,6 +91,9 @@ def assert_verify_equal(res, ref, what):
     dq = np.abs(res["q_tok"] - ref["q_tok"]).max()
     assert dp <= 1e-5 and dq <= 1e-5, (what, dp, dq)
     assert ties.sum() <= max(1, B // 10), (what, "near-ties", int(ties.sum()))
+    # at least one sequence is compared bit for bit (a single-sequence case
+    # whose only sequence is a near-tie would otherwise compare nothing)
+    assert ok.any(), (what, "every sequence was a near-tie: nothing compared")
     log(f"  {what}: B={B} near-tie sequences={int(ties.sum())} max|dp|={dp:.2e} "
         f"max|dq|={dq:.2e} acc_len mean={res['acc_len'].mean():.2f}")
 

@@ -36,10 +36,12 @@ SIGNATURES = {
                                                                  _vp]),
     "spec_verify_workspace_size": (_c_size, [_c_int] * 5),
     "spec_verify": (_c_int, [_c_int] * 5 + [_vp] * 17 + [_c_size, _vp, _vp]),
-    "spec_kv_compact": (_c_int, [_c_int] * 6 + [_vp] * 7),
+    "spec_kv_compact_workspace_size": (_c_size, [_c_int]),
+    "spec_kv_compact": (_c_int, [_c_int] * 6 + [_vp] * 6 + [_c_size, _vp, _vp]),
     "spec_beam_topk_workspace_size": (_c_size, [_c_int] * 4),
     "spec_beam_topk": (_c_int, [_c_int] * 4 + [_vp] * 6 + [_c_int, _vp, _vp, _c_size, _vp]),
     "spec_select_tree": (_c_int, [_c_int] * 3 + [_vp] * 9),
+    "spec_last_device_status": (_c_int, [_vp, _vp]),
     "spec_copy_probe": (_c_int, [_vp, _vp, _c_size, _vp]),
 }
 
@@ -132,11 +134,15 @@ def spec_verify(mode, B, T_cap, V, R, tgt, dft, dft_row, n_nodes, parent, token,
     _check("spec_verify", rc)
 
 
+def spec_kv_compact_workspace_size(B) -> int:
+    return load().spec_kv_compact_workspace_size(B)
+
+
 def spec_kv_compact(dt, B, Hkv, D, cache_cap, T_cap, k_cache, v_cache, ctx_len, acc_len,
-                    acc_path, status=None, stream=None):
+                    acc_path, ws, ws_bytes, status=None, stream=None):
     rc = load().spec_kv_compact(dt, B, Hkv, D, cache_cap, T_cap, _ptr(k_cache), _ptr(v_cache),
-                                _ptr(ctx_len), _ptr(acc_len), _ptr(acc_path), _ptr(status),
-                                _stream(stream))
+                                _ptr(ctx_len), _ptr(acc_len), _ptr(acc_path), _ptr(ws),
+                                ws_bytes, _ptr(status), _stream(stream))
     _check("spec_kv_compact", rc)
 
 
@@ -163,6 +169,16 @@ def spec_select_tree(B, N, N_keep, cand_parent, cand_token, cand_logp, keep_pare
 def spec_copy_probe(src, dst, n_bytes, stream=None):
     rc = load().spec_copy_probe(_ptr(src), _ptr(dst), n_bytes, _stream(stream))
     _check("spec_copy_probe", rc)
+
+
+def spec_last_device_status(status=None, stream=None) -> int:
+    """SPEC_DEV_* bits of a device status word (the library's own word when
+    status is None) once the stream has finished; the library's word is
+    cleared after it is read."""
+    rc = load().spec_last_device_status(_ptr(status), _stream(stream))
+    if rc < 0:
+        raise SpecError("spec_last_device_status", rc)
+    return rc
 
 
 def decode_status(word: int) -> list[str]:

@@ -192,6 +192,7 @@ extern "C" int spec_build_tree(int kind, int B, int W, int L, int T_cap,
                        root_token, n_nodes, parent, token, depth, anc, beam_node);
   } else if (kind == SPEC_TREE_EXPLICIT) {
     if (!cand_parent || beam_node) return SPEC_ERR_INVALID;
+    status = status_or_library(status);
     hipLaunchKernelGGL(k_build_explicit, dim3(B), dim3(kThreads), 0, s, W * L, T_cap,
                        cand_token, cand_parent, root_token, n_nodes, parent, token, depth, anc,
                        status);

@@ -133,6 +133,10 @@ __device__ inline void wave_argmax(float& m, int& a) {
 }
 
 // ---------------------------------------------------------------- host side
+// The caller's status word, or the library's own word on the current device
+// when the caller passes none (status.hip).
+int32_t* status_or_library(int32_t* status);
+
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }

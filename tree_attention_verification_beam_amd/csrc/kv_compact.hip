@@ -15,21 +15,23 @@ namespace spec {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kArrive = 1 << 24;  // arrival count lives above the context length
+constexpr int kBatch = 4;                     // 16-byte loads in flight per thread
+constexpr long kBufWords = 64 * 1024 / 16;    // LDS buffer of a workgroup: 64 KiB
 
 // One workgroup per (sequence, K or V, group of HPG KV heads), sized on the
-// host so that the longest possible path of a group fits its LDS buffer.  Few
-// workgroups per sequence keep the arrival count below (one same-address
-// atomic per workgroup) cheap.  Every workgroup of a sequence
-// first adds kArrive to ctx_len[b] atomically: the low 24 bits of the returned
-// value are the context length before the commit, whatever the arrival order,
-// and the workgroup that arrives last writes the new length (all others have
-// read the old one by then).
+// host so that the longest possible path of a group fits its LDS buffer; about
+// 64 groups overall, so a small batch still spreads its rows over many CUs.
+// Every workgroup of a sequence reads the context length, then adds one to the
+// sequence's arrival counter in the workspace (after the read has returned);
+// the workgroup that arrives last has seen every other arrival, so every other
+// workgroup has read the old length by then: it writes the new length and
+// returns the counter to zero for the next call.  ctx_len holds nothing but
+// the length at any time.
 __global__ __launch_bounds__(kThreads) void k_kv_compact(
     int elem_bytes, int Hkv, int HPG, int G, int D, int cache_cap, int T_cap,
     unsigned char* __restrict__ kc, unsigned char* __restrict__ vc, int32_t* __restrict__ ctx_len,
     const int32_t* __restrict__ acc_len, const int32_t* __restrict__ acc_path,
-    int32_t* __restrict__ status) {
+    uint32_t* __restrict__ arrivals, int32_t* __restrict__ status) {
   static_assert(kThreads >= SPEC_MAX_TREE, "one path entry per thread");
   extern __shared__ uint4 buf[];  // [HPG * longest path * row words]
   __shared__ int s_src[SPEC_MAX_TREE];
@@ -38,17 +40,20 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
   const int which = blockIdx.y / G;
   const int g = blockIdx.y - which * G;
   const int tid = threadIdx.x;
+  // the length, the accepted count and the whole path row in one round trip;
+  // entries past the accepted length are ignored
   const int n = acc_len[b];
   const int32_t* path = acc_path + (size_t)b * T_cap;
-  // the whole path row is read with the length and the arrival count, in one
-  // round trip; entries past the accepted length are ignored
   const int my_src = tid < T_cap ? path[tid] : 0;
   if (tid == 0) {
-    const int old = atomicAdd(ctx_len + b, kArrive);
-    const int ctx = old & (kArrive - 1);
+    const int ctx = __hip_atomic_load(ctx_len + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the length has arrived before the arrival is counted
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    const uint32_t before = __hip_atomic_fetch_add(arrivals + b, 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
     s_ctx = ctx;
-    s_last = (old >> 24) == 2 * G - 1;
-    s_ok = (n >= 0 && n < T_cap && ctx + n + 1 <= cache_cap) ? 1 : 0;
+    s_last = before == (uint32_t)(2 * G - 1);
+    s_ok = (n >= 0 && n < T_cap && ctx >= 0 && ctx + n + 1 <= cache_cap) ? 1 : 0;
   }
   if (tid < T_cap) s_src[tid] = my_src;
   __syncthreads();
@@ -70,7 +75,6 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
     // kBatch loads in flight per thread: every load is issued (a unit past the
     // end reads the group's first word as a stand-in) and only the LDS store
     // is predicated, so the loads do not wait on one another
-    constexpr int kBatch = 4;
     auto unit = [&](int e, bool& keep) -> uint4 {
       const bool in = e < total;
       const int ec = in ? e : 0;
@@ -82,16 +86,14 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
       return *reinterpret_cast<const uint4*>(base + off);
     };
     for (int e0 = tid; e0 < total; e0 += kBatch * kThreads) {
-      bool k0, k1, k2, k3;
-      const uint4 t0 = unit(e0, k0);
-      const uint4 t1 = unit(e0 + kThreads, k1);
-      const uint4 t2 = unit(e0 + 2 * kThreads, k2);
-      const uint4 t3 = unit(e0 + 3 * kThreads, k3);
+      uint4 t[kBatch];
+      bool keep[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) t[k] = unit(e0 + k * kThreads, keep[k]);
       __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of its stores
-      if (k0) buf[e0] = t0;
-      if (k1) buf[e0 + kThreads] = t1;
-      if (k2) buf[e0 + 2 * kThreads] = t2;
-      if (k3) buf[e0 + 3 * kThreads] = t3;
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (keep[k]) buf[e0 + k * kThreads] = t[k];
     }
     __syncthreads();  // every source read before any destination is written
     for (int e = tid; e < total; e += kThreads) {
@@ -104,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void k_kv_compact(
   }
   if (tid == 0 && s_last) {
     // every other workgroup of the sequence has read the old length already
-    atomicExch(ctx_len + b, s_ok ? ctx + n + 1 : ctx);
+    ctx_len[b] = s_ok ? ctx + n + 1 : ctx;
+    __hip_atomic_store(arrivals + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!s_ok) raise_status(status, SPEC_DEV_CTX_RANGE);
   }
 }
@@ -122,24 +125,27 @@ __global__ __launch_bounds__(256) void k_copy_probe(const uint4* __restrict__ sr
 
 using namespace spec;
 
+extern "C" size_t spec_kv_compact_workspace_size(int B) {
+  return B < 1 ? 0 : round_up((size_t)B * sizeof(uint32_t), 256);
+}
+
 extern "C" int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int T_cap,
                                void* k_cache, void* v_cache, int32_t* ctx_len,
-                               const int32_t* acc_len, const int32_t* acc_path, int32_t* status,
-                               void* stream) {
+                               const int32_t* acc_len, const int32_t* acc_path, void* ws,
+                               size_t ws_bytes, int32_t* status, void* stream) {
   if (B < 0 || Hkv < 1 || D < 1 || cache_cap < 1 || T_cap < 1) return SPEC_ERR_INVALID;
   if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
   const int eb = dt == SPEC_F32 ? 4 : dt == SPEC_BF16 ? 2 : 0;
   if (!eb) return SPEC_ERR_INVALID;
   if ((D * eb) % 16) return SPEC_ERR_UNSUPPORTED;
-  if (cache_cap >= kArrive) return SPEC_ERR_UNSUPPORTED;  // lengths share a word with a count
-  if (2 * Hkv > 127) return SPEC_ERR_UNSUPPORTED;
+  // heads per workgroup: the longest path a group can commit fits 64 KiB of LDS
+  const long per_head_max = (long)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb / 16;
+  if (per_head_max > kBufWords) return SPEC_ERR_UNSUPPORTED;
   if (B == 0) return SPEC_OK;
   if (!k_cache || !v_cache || !ctx_len || !acc_len || !acc_path) return SPEC_ERR_INVALID;
   if (!aligned(k_cache, 16) || !aligned(v_cache, 16)) return SPEC_ERR_INVALID;
-  // heads per workgroup: the longest path a group can commit fits 64 KiB of LDS
-  constexpr long kBufWords = 64 * 1024 / 16;
-  const long per_head_max = (long)(T_cap - 1 > 0 ? T_cap - 1 : 1) * D * eb / 16;
-  if (per_head_max > kBufWords) return SPEC_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < spec_kv_compact_workspace_size(B) || !aligned(ws, 256))
+    return SPEC_ERR_WORKSPACE;
   int HPG = (int)(kBufWords / per_head_max);
   if (HPG > Hkv) HPG = Hkv;
   // small batches get more groups (more workgroups in flight), large ones
@@ -149,9 +155,11 @@ extern "C" int spec_kv_compact(int dt, int B, int Hkv, int D, int cache_cap, int
   if (g_want > g_min) HPG = (Hkv + g_want - 1) / g_want;
   const int G = (Hkv + HPG - 1) / HPG;
   const size_t lds = (size_t)HPG * per_head_max * 16;
+  status = status_or_library(status);
   hipLaunchKernelGGL(k_kv_compact, dim3(B, 2 * G), dim3(kThreads), lds, as_stream(stream), eb,
                      Hkv, HPG, G, D, cache_cap, T_cap, static_cast<unsigned char*>(k_cache),
-                     static_cast<unsigned char*>(v_cache), ctx_len, acc_len, acc_path, status);
+                     static_cast<unsigned char*>(v_cache), ctx_len, acc_len, acc_path,
+                     static_cast<uint32_t*>(ws), status);
   return launch_status();
 }
 

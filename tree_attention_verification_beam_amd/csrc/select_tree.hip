@@ -190,6 +190,7 @@ extern "C" int spec_select_tree(int B, int N, int N_keep, const int32_t* cand_pa
   if (B == 0) return SPEC_OK;
   if (!cand_parent || !cand_token || !cand_logp || !keep_parent || !keep_token)
     return SPEC_ERR_INVALID;
+  status = status_or_library(status);
   hipLaunchKernelGGL(k_select_tree, dim3(B), dim3(kSelTreeThreads), 0, as_stream(stream), N,
                      N_keep, cand_parent, cand_token, cand_logp, keep_parent, keep_token,
                      keep_src, keep_score, status);

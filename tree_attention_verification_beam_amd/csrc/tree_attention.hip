@@ -955,6 +955,7 @@ extern "C" int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int
   if (!q || !k_cache || !v_cache || !ctx_len || !n_nodes || !anc || !out) return SPEC_ERR_INVALID;
   if (!(scale > 0.0f)) scale = 1.0f / sqrtf((float)D);
   hipStream_t s = as_stream(stream);
+  status = status_or_library(status);
   if (dt == SPEC_F32) {
     if (D > 256) return SPEC_ERR_UNSUPPORTED;
     const int rows = B * T_cap * H;

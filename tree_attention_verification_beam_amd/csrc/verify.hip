@@ -1120,7 +1120,8 @@ extern "C" size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, 
   if (mode == SPEC_GREEDY_WALK && B >= 1) return verify_walk_workspace_size(B);
   if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE || B < 1 || T_cap < 1 || V < 1)
     return 0;
-  return make_plan(mode, B, T_cap, V, R).total;
+  const VerifyPlan pl = make_plan(mode, B, T_cap, V, R);
+  return pl.n_chunks > kMergeEntries ? 0 : pl.total;
 }
 
 extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float* tgt,
@@ -1136,6 +1137,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   if (B == 0) return SPEC_OK;
   if (!tgt || !n_nodes || !parent || !token || !depth || !acc_len || !acc_path || !next_token)
     return SPEC_ERR_INVALID;
+  status = status_or_library(status);
   if (mode == SPEC_GREEDY_WALK)
     return launch_verify_walk(B, T_cap, V, tgt, n_nodes, parent, token, depth, acc_len,
                               acc_path, next_token, p_tok, q_tok, decision, near_tie, ws,
@@ -1144,6 +1146,9 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
     if (!dft || !dft_row || R < 1 || !u_node || !u_final) return SPEC_ERR_INVALID;
   }
   const VerifyPlan pl = make_plan(mode, B, T_cap, V, R);
+  // a row's chunk partials are merged in LDS batches of kMergeEntries: a
+  // vocabulary with more chunks than that (V > 32 * 256 * 1024) is refused
+  if (pl.n_chunks > kMergeEntries) return SPEC_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < pl.total || !aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
   char* w = static_cast<char*>(ws);

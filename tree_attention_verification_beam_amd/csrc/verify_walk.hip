@@ -16,24 +16,23 @@
 // k_vwalk: P workgroups per sequence split every scanned row into P slices (a
 // single CU streams only some 20 GB/s from HBM, so one row needs many CUs).
 // Each scan ends in a meeting of the P workgroups: each publishes its slice's
-// (max, argmax) and sum through agent-coherent stores, waits for its stores,
-// adds one to the sequence's arrival counter and waits until the counter
-// reaches P times the number of meetings so far; then every workgroup combines
-// the P entries in the same order and takes the same decisions.  Entries of
-// meeting r sit in parity r & 1: meeting r + 2 overwrites them only after all
-// P workgroups have arrived at meeting r + 1, i.e. after every reader is done
-// with meeting r.  After the last meeting the lead workgroup resets the
-// counter; a workgroup still waiting at that meeting sees it fall to or below
-// the value it had before the meeting, which only the reset can cause, and
-// takes that as completion.  So each call leaves its workspace ready for the
-// next (it must be zero before the first call; the entry words need no
-// clearing, as a meeting reads them only after all P have been written).
-// The grid is sized to be resident at once (occupancy query) and every wait
-// is bounded.
+// (max, argmax, sum) as four 64-bit words, 32 bits of payload beside a 32-bit
+// tag made of the call's epoch (a host counter, new for every call) and the
+// meeting's number, and one wave then polls the 4P words of the meeting until
+// every tag matches; every workgroup combines the P entries in the same order
+// and takes the same decisions.  Entries of meeting r sit in parity r & 1:
+// meeting r + 2 overwrites them only after all P workgroups have published
+// meeting r + 1, i.e. after every reader is done with meeting r.  Words left
+// by an earlier call, even one that ended at a wait bound with late
+// workgroups still publishing, carry another epoch and never match, so the
+// workspace needs no initial contents and no reset.  The grid is sized to be
+// resident at once (occupancy query) and every wait is bounded.
 //
 // A slice scan keeps two batches of 16-byte buffer loads in flight; loads past
 // the slice end return zeros and are masked to -inf.  The logits of the tested
 // children's own tokens are gathered while the row streams, for p_tok.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace spec {
@@ -53,12 +52,12 @@ constexpr int kWalkMaxP = 32;
 constexpr int kBatch = 8;  // 16-byte loads per thread per batch (two batches in flight)
 constexpr float kLog2eW = 1.4426950408889634f;
 constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3, raw 32-bit loads
-// per sequence: the arrival counter (in a 64-byte header), then
-// [2 parities][P][2] entry words
-constexpr size_t kWalkStride = 64 + 2 * kWalkMaxP * 2 * 8;
+// per sequence: [2 parities][P][4] tagged entry words
+constexpr size_t kWalkStride = 2 * kWalkMaxP * 4 * 8;
 
 struct WalkArgs {
   int B, T_cap, V, P, slice;  // slice: vocabulary entries per workgroup (multiple of 4)
+  uint32_t epoch;             // this call's tag base (bits 8..31), never 0
   const float* tgt;
   const int32_t* n_nodes;
   const int32_t* parent;
@@ -222,46 +221,63 @@ __device__ void slice_finish(const float* row, int base, int n, __amdgpu_buffer_
 
 // Meeting `round` of the P workgroups of a sequence: publish this workgroup's
 // (M, arg, S), wait for all P, combine them in workgroup order (the same result
-// in every workgroup) into sh.M, sh.arg, sh.S.
-__device__ void meet(uint64_t* seq, int P, int w, int round, WalkShared& sh, int32_t* status) {
+// in every workgroup) into sh.M, sh.arg, sh.S.  Word k of a workgroup's entry
+// holds 32 bits of its values in the low half and the tag epoch | round in the
+// high half, so a word read at the coherent level with the current tag belongs
+// to this meeting, whatever order the stores landed in.
+__device__ void meet(uint64_t* seq, int P, int w, uint32_t epoch, int round, WalkShared& sh,
+                     int32_t* status) {
   if (P == 1) return;
-  uint64_t* arrive = seq;
-  uint64_t* entries = seq + 8 + (size_t)(round & 1) * kWalkMaxP * 2;
-  if (threadIdx.x == 0) {
-    const uint64_t ma = ((uint64_t)__float_as_uint(sh.M) << 32) | (uint32_t)sh.arg;
-    store_coherent(entries + 2 * w, ma);
-    store_coherent(entries + 2 * w + 1, (uint64_t)__double_as_longlong(sh.S));
-    wait_stores_done();
-    const uint64_t base = (uint64_t)round * P;  // the counter before this meeting
-    const uint64_t target = base + P;
-    const uint64_t old =
-        __hip_atomic_fetch_add(arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1 < target) {  // (the last to arrive does not wait)
-      int spins = 0;
-      for (;;) {
-        const uint64_t v = load_coherent(arrive);
-        // v <= base: the lead has reset the counter after the last meeting,
-        // which it does only once all P have arrived at it
-        if (v >= target || v <= base) break;
-        __builtin_amdgcn_s_sleep(1);  // back off: P pollers share the counter's line
-        if (++spins > (1 << 22)) {
-          raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
-          break;
-        }
-      }
-    }
-  }
-  __syncthreads();
+  uint64_t* entries = seq + (size_t)(round & 1) * kWalkMaxP * 4;
+  const uint64_t tag = (uint64_t)(epoch | (uint32_t)(round & 0xff)) << 32;
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
+    if (lane < 4) {
+      const uint64_t sbits = (uint64_t)__double_as_longlong(sh.S);
+      const uint32_t half = lane == 0   ? __float_as_uint(sh.M)
+                            : lane == 1 ? (uint32_t)sh.arg
+                            : lane == 2 ? (uint32_t)sbits
+                                        : (uint32_t)(sbits >> 32);
+      store_coherent(entries + 4 * w + lane, tag | half);
+    }
+    // the 4P words of this parity, two per lane
+    const int n = 4 * P;
+    uint64_t v0 = 0, v1 = 0;
+    bool ok0 = lane >= n, ok1 = lane + 64 >= n;
+    int spins = 0;
+    while (!(ok0 && ok1)) {
+      if (!ok0) {
+        v0 = load_coherent(entries + lane);
+        ok0 = (v0 & 0xffffffff00000000ull) == tag;
+      }
+      if (!ok1) {
+        v1 = load_coherent(entries + lane + 64);
+        ok1 = (v1 & 0xffffffff00000000ull) == tag;
+      }
+      if (++spins > (1 << 22)) {
+        raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
+        break;
+      }
+    }
+    // lane 4i + k holds word k of workgroup i (lanes 0..63: workgroups 0..15,
+    // lanes 64.. of the second word: workgroups 16..31); gather workgroup
+    // `lane`'s words with cross-lane reads
+    const uint32_t lo0 = (uint32_t)v0, lo1 = (uint32_t)v1;
+    const int src = 4 * (lane & 15);
+    uint32_t wd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t x0 = (uint32_t)__shfl((int)lo0, src + k);
+      const uint32_t x1 = (uint32_t)__shfl((int)lo1, src + k);
+      wd[k] = lane < 16 ? x0 : x1;
+    }
     float m = -INFINITY;
     int a = 0x7fffffff;
     double S = 0.0;
     if (lane < P) {
-      const uint64_t ma = load_coherent(entries + 2 * lane);
-      m = __uint_as_float((uint32_t)(ma >> 32));
-      a = (int)(uint32_t)ma;
-      S = __longlong_as_double((long long)load_coherent(entries + 2 * lane + 1));
+      m = __uint_as_float(wd[0]);
+      a = (int)wd[1];
+      S = __longlong_as_double((long long)(((uint64_t)wd[3] << 32) | wd[2]));
     }
     float M = m;
     int A = a;
@@ -352,7 +368,7 @@ __global__ __launch_bounds__(kWalkThreads) void k_vwalk(WalkArgs A) {
       const bool child = tid >= 1 && tid < T && sh.par[tid] == f;
       const float lx = child ? row[sh.tok[tid]] : 0.0f;
       slice_finish<VEC>(row, base, n, rs, L, sh);
-      meet(seq, P, w, round++, sh, A.status);
+      meet(seq, P, w, A.epoch, round++, sh, A.status);
       if (tid == 0) sh.greedy[f] = sh.arg < V ? sh.arg : 0;  // every logit -inf: index 0
       if (child) {
         sh.dec[tid] = sh.tok[tid] == sh.arg;
@@ -378,9 +394,6 @@ __global__ __launch_bounds__(kWalkThreads) void k_vwalk(WalkArgs A) {
   }
 
   // ---------------------------------------------------------------- leave
-  // the lead resets the arrival counter: it is past the last meeting, so all P
-  // have arrived there, and one still waiting reads the reset as completion
-  if (P > 1 && lead && tid == 0) store_coherent(seq, 0ull);
   if (!lead) return;
 
   // ---------------------------------------------------------------- outputs
@@ -448,7 +461,13 @@ int launch_verify_walk(int B, int T_cap, int V, const float* tgt, const int32_t*
   const int P = choose_walk_p(B, V);
   int slice = (V + P - 1) / P;
   slice = (slice + 3) & ~3;  // slices start on 16-byte boundaries of 16-byte-aligned rows
+  // a new tag base for every call: bits 8..31 of the tag, never 0 (a
+  // zero-filled workspace never matches)
+  static std::atomic<uint32_t> calls{0};
+  uint32_t e = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0xffffffu;
+  if (e == 0) e = 1;
   WalkArgs A{};
+  A.epoch = e << 8;
   A.B = B;
   A.T_cap = T_cap;
   A.V = V;
@@ -473,12 +492,12 @@ int launch_verify_walk(int B, int T_cap, int V, const float* tgt, const int32_t*
                        : reinterpret_cast<const void*>(k_vwalk<false>);
   void* args[] = {&A};
   const dim3 grid((unsigned)(B * P));
-  hipError_t e;
+  hipError_t err;
   if (P > 1)
-    e = launch_meeting_kernel(fn, grid, dim3(kWalkThreads), args, s);
+    err = launch_meeting_kernel(fn, grid, dim3(kWalkThreads), args, s);
   else
-    e = hipLaunchKernel(fn, grid, dim3(kWalkThreads), args, 0, s);
-  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+    err = hipLaunchKernel(fn, grid, dim3(kWalkThreads), args, 0, s);
+  return err == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
 }  // namespace spec

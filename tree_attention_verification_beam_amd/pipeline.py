@@ -94,9 +94,14 @@ class Step:
         self.decision = torch.zeros((B, T_cap), dtype=torch.int8, device=dev)
         self.near_tie = torch.zeros(B, **i32)
         nb = sv.spec_verify_workspace_size(self.mode, B, T_cap, V, self.R)
-        # zero-filled once (the greedy walk's meeting counters start at zero)
+        # no initial contents are needed; zero-filled for reproducible tests
         self.ver_ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=dev)
         self.ver_ws_bytes = nb
+        # the commit's arrival counters: zero before the first call, and every
+        # call leaves them at zero
+        nc = sv.spec_kv_compact_workspace_size(B)
+        self.cmp_ws = torch.zeros(max(nc, 256), dtype=torch.uint8, device=dev)
+        self.cmp_ws_bytes = nc
 
     # ------------------------------------------------------------------ prepared calls
     def prepare(self, stream=None):
@@ -120,9 +125,26 @@ class Step:
                                  self.attn_ws, self.attn_ws_bytes, self.status, stream=stream)
             self.p_compact = P("spec_kv_compact", self.dt, self.B, self.Hkv, self.D, self.cap,
                                self.T_cap, self.k, self.v, self.ctx_len, self.acc_len,
-                               self.acc_path, self.status, stream=stream)
+                               self.acc_path, self.cmp_ws, self.cmp_ws_bytes, self.status,
+                               stream=stream)
             self.p_reset = P("spec_copy_probe", self.ctx0, self.ctx_len, self.ctx_bytes,
                              stream=stream)
+
+    def prepare_verify_mode(self, mode: str, stream=None):
+        """spec_verify in another mode on this step's tree and rows, with a
+        workspace of its own (outputs shared with the step's own verify call),
+        for timing the modes side by side."""
+        m = sv.MODES[mode]
+        R = self.R if m not in (sv.SPEC_GREEDY, sv.SPEC_GREEDY_WALK) else 0
+        nb = sv.spec_verify_workspace_size(m, self.B, self.T_cap, self.V, R)
+        ws = torch.zeros(max(nb, 256), dtype=torch.uint8, device=self.device)
+        call = sv.prepare("spec_verify", m, self.B, self.T_cap, self.V, R, self.tgt,
+                          self.dft if R else None, self.dft_row if R else None, self.n_nodes,
+                          self.parent, self.token, self.depth, self.u_node, self.u_final,
+                          self.acc_len, self.acc_path, self.next_token, self.p_tok, self.q_tok,
+                          self.decision, self.near_tie, ws, nb, self.status, stream=stream)
+        call.workspace = ws  # keep it alive with the call
+        return call
 
     def prepare_fresh_contexts(self, n, stream=None):
         """n copies of the initial context lengths, each with its own prepared
@@ -139,7 +161,8 @@ class Step:
             for c in self.fresh_ctx]
         self.p_compact_fresh = [
             P("spec_kv_compact", self.dt, self.B, self.Hkv, self.D, self.cap, self.T_cap, self.k,
-              self.v, c, self.acc_len, self.acc_path, self.status, stream=stream)
+              self.v, c, self.acc_len, self.acc_path, self.cmp_ws, self.cmp_ws_bytes,
+              self.status, stream=stream)
             for c in self.fresh_ctx]
 
     # ------------------------------------------------------------------ calls
@@ -163,7 +186,8 @@ class Step:
 
     def compact(self, stream=None):
         sv.spec_kv_compact(self.dt, self.B, self.Hkv, self.D, self.cap, self.T_cap, self.k, self.v,
-                           self.ctx_len, self.acc_len, self.acc_path, self.status, stream)
+                           self.ctx_len, self.acc_len, self.acc_path, self.cmp_ws,
+                           self.cmp_ws_bytes, self.status, stream)
 
     def launch(self, compact: bool = True, stream=None):
         """Enqueue one whole step (no host synchronisation)."""
