@@ -220,6 +220,28 @@ int spec_verify(int mode, int B, int T_cap, int V, int R, const float *tgt, cons
                 size_t ws_bytes, int32_t *status, void *stream);
 
 /*
+ * spec_verify_noalloc -- spec_verify with the library's own workspace, for
+ * callers that cannot allocate device memory (code under stream capture, tight
+ * serving loops, harnesses that forbid allocation).
+ *
+ * Arguments, outputs and device status are spec_verify's, without ws and
+ * ws_bytes.  The workspace is a 4 MiB device array inside the library, one per
+ * device, held until the process ends; the call itself allocates nothing.
+ * Returns SPEC_ERR_CAPACITY (nothing launched) when
+ * spec_verify_workspace_size() for the arguments exceeds 4 MiB (4194304
+ * bytes), and SPEC_ERR_HIP if the array's address cannot be obtained.  Every
+ * call on one device shares that device's array: calls that overlap in time
+ * on one device (on different streams, or from different host threads) race
+ * and must not be issued.
+ */
+int spec_verify_noalloc(int mode, int B, int T_cap, int V, int R, const float *tgt,
+                        const float *dft, const int32_t *dft_row, const int32_t *n_nodes,
+                        const int32_t *parent, const int32_t *token, const int32_t *depth,
+                        const float *u_node, const float *u_final, int32_t *acc_len,
+                        int32_t *acc_path, int32_t *next_token, float *p_tok, float *q_tok,
+                        int8_t *decision, int32_t *near_tie, int32_t *status, void *stream);
+
+/*
  * spec_kv_compact -- commit the accepted path's K/V to contiguous cache slots.
  *
  * [ReDrafter] Step 6: the accepted tokens join the context and the next step

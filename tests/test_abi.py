@@ -140,3 +140,12 @@ def test_compact_refuses_a_path_beyond_its_buffer(lib):
     assert cdll.spec_kv_compact(0, 1, 8, 128, 10000, 128, *ptrs, None, 0, None, None) == -4
     assert cdll.spec_kv_compact(0, 300, 8, 128, 10000, 128, *ptrs, 256, 256, None, None) == -4
     assert cdll.spec_kv_compact_workspace_size(300) == 1280
+
+
+def test_verify_noalloc_refuses_beyond_its_array(lib):
+    """The no-allocation verify takes at most 4 MiB of workspace from the
+    library's own device array; a larger need is refused on the host."""
+    cdll = lib.load()
+    assert cdll.spec_verify_workspace_size(3, 4096, 17, 1000, 0) > 4 << 20
+    assert cdll.spec_verify_noalloc(3, 4096, 17, 1000, 0, *([16] * 16), None, None) == -3
+    assert cdll.spec_verify_noalloc(0, 0, 17, 1000, 0, *([None] * 16), None, None) == 0

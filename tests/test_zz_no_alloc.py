@@ -1,0 +1,67 @@
+"""The no-allocation verify entry point against the workspace one, through the
+C ABI: spec_verify_noalloc (the library's own device array as workspace) must
+give spec_verify's outputs bit for bit (the same kernels), on two calls in a
+row in every mode, the second call on a smaller input than the first (the
+array keeps the first call's contents)."""
+import numpy as np
+import pytest
+import torch
+
+from tree_attention_verification_beam_amd import binding as sv
+from tree_attention_verification_beam_amd import pipeline, synth
+
+pytestmark = pytest.mark.gpu
+
+OUTS = ("acc_len", "acc_path", "next_token", "p_tok", "q_tok", "decision", "near_tie")
+
+# (workload, overrides) of the first, larger call and of the second, smaller one
+CASES = {
+    "greedy": ((2, dict(ctx_override=64)), (1, dict(ctx_override=64))),
+    "greedy_walk": ((2, dict(ctx_override=64)), (1, dict(ctx_override=64))),
+    "reject_path": ((3, dict(B_override=16, ctx_override=64)), (0, {})),
+    "reject_recursive": ((4, dict(ctx_override=64)), (4, dict(B_override=1, ctx_override=64))),
+}
+
+
+def run_pair(step, mode_id):
+    """spec_verify (the step's workspace) and spec_verify_noalloc on the same
+    tree and rows; returns both outputs as numpy dicts."""
+    step.build_tree()
+    step.verify()
+    torch.cuda.synchronize()
+    ref = {k: getattr(step, k).cpu().numpy().copy() for k in OUTS}
+    for k in OUTS:
+        getattr(step, k).fill_(-7)
+    status = torch.zeros(1, dtype=torch.int32, device=step.device)
+    sv.spec_verify_noalloc(mode_id, step.B, step.T_cap, step.V, step.R, step.tgt, step.dft,
+                           step.dft_row, step.n_nodes, step.parent, step.token, step.depth,
+                           step.u_node, step.u_final, step.acc_len, step.acc_path,
+                           step.next_token, step.p_tok, step.q_tok, step.decision,
+                           step.near_tie, status)
+    torch.cuda.synchronize()
+    got = {k: getattr(step, k).cpu().numpy().copy() for k in OUTS}
+    return ref, got, int(status.item()), int(step.status.item())
+
+
+@pytest.mark.parametrize("mode", list(CASES))
+def test_noalloc_matches_workspace_call(gpu, mode):
+    mode_id = sv.MODES[mode]
+    for call, (wid, ov) in enumerate(CASES[mode]):
+        inp = synth.make_inputs(wid, 500 + call, **ov)
+        print(f"case no-alloc {mode} call {call}: workload {wid} B={inp['B']} V={inp['V']}",
+              flush=True)
+        step = pipeline.Step(inp, mode, with_kv=False)
+        ref, got, st_noalloc, st_ref = run_pair(step, mode_id)
+        assert st_noalloc == 0 and st_ref == 0, (st_noalloc, st_ref)
+        for k in OUTS:
+            assert np.array_equal(ref[k], got[k]), (mode, call, k)
+        assert ref["acc_len"].shape[0] == inp["B"]
+
+
+def test_noalloc_refuses_beyond_its_array(gpu):
+    """A workspace need beyond the 4 MiB array is refused before any launch."""
+    big_B = 4096  # the walk needs 2 KiB per sequence: 8 MiB
+    assert sv.spec_verify_workspace_size(sv.SPEC_GREEDY_WALK, big_B, 17, 1000, 0) > 4 << 20
+    rc = sv.load().spec_verify_noalloc(sv.SPEC_GREEDY_WALK, big_B, 17, 1000, 0, *([16] * 16),
+                                       None, None)
+    assert rc == -3

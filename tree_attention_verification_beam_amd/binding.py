@@ -36,6 +36,7 @@ SIGNATURES = {
                                                                  _vp]),
     "spec_verify_workspace_size": (_c_size, [_c_int] * 5),
     "spec_verify": (_c_int, [_c_int] * 5 + [_vp] * 17 + [_c_size, _vp, _vp]),
+    "spec_verify_noalloc": (_c_int, [_c_int] * 5 + [_vp] * 16 + [_vp, _vp]),
     "spec_kv_compact_workspace_size": (_c_size, [_c_int]),
     "spec_kv_compact": (_c_int, [_c_int] * 6 + [_vp] * 6 + [_c_size, _vp, _vp]),
     "spec_beam_topk_workspace_size": (_c_size, [_c_int] * 4),
@@ -132,6 +133,17 @@ def spec_verify(mode, B, T_cap, V, R, tgt, dft, dft_row, n_nodes, parent, token,
                             _ptr(p_tok), _ptr(q_tok), _ptr(decision), _ptr(near_tie), _ptr(ws),
                             ws_bytes, _ptr(status), _stream(stream))
     _check("spec_verify", rc)
+
+
+def spec_verify_noalloc(mode, B, T_cap, V, R, tgt, dft, dft_row, n_nodes, parent, token, depth,
+                        u_node, u_final, acc_len, acc_path, next_token, p_tok, q_tok, decision,
+                        near_tie, status=None, stream=None):
+    rc = load().spec_verify_noalloc(mode, B, T_cap, V, R, _ptr(tgt), _ptr(dft), _ptr(dft_row),
+                                    _ptr(n_nodes), _ptr(parent), _ptr(token), _ptr(depth),
+                                    _ptr(u_node), _ptr(u_final), _ptr(acc_len), _ptr(acc_path),
+                                    _ptr(next_token), _ptr(p_tok), _ptr(q_tok), _ptr(decision),
+                                    _ptr(near_tie), _ptr(status), _stream(stream))
+    _check("spec_verify_noalloc", rc)
 
 
 def spec_kv_compact_workspace_size(B) -> int:

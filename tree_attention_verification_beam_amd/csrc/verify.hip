@@ -26,6 +26,8 @@
 //             then holds the same totals and takes the same decisions.  The
 //             grid is sized to be resident at once (occupancy query) and every
 //             wait is bounded.
+#include <mutex>
+
 #include "common.hpp"
 
 namespace spec {
@@ -1211,4 +1213,61 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   else
     e = hipLaunchKernel(fn, grid, dim3(kSelThreads), args, 0, s);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+// ------------------------------------------------------------------ no-allocation variant
+// spec_verify for callers that cannot allocate (code under stream capture,
+// tight serving loops): the workspace is a file-scope device array of
+// kNoAllocScratchBytes, one per device, held until the process ends.  Host
+// code never passes the array's name to a kernel (on the host it only stands
+// for the symbol): its device address is looked up once per device with that
+// device current and kept.
+
+namespace {
+constexpr size_t kNoAllocScratchBytes = 4u << 20;  // every mode of every workload above fits
+constexpr int kNoAllocMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kNoAllocMaxDevices];
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int spec_verify_noalloc(int mode, int B, int T_cap, int V, int R, const float* tgt,
+                                   const float* dft, const int32_t* dft_row,
+                                   const int32_t* n_nodes, const int32_t* parent,
+                                   const int32_t* token, const int32_t* depth,
+                                   const float* u_node, const float* u_final, int32_t* acc_len,
+                                   int32_t* acc_path, int32_t* next_token, float* p_tok,
+                                   float* q_tok, int8_t* decision, int32_t* near_tie,
+                                   int32_t* status, void* stream) {
+  if (mode < SPEC_GREEDY || mode > SPEC_GREEDY_WALK) return SPEC_ERR_INVALID;
+  if (B < 0 || T_cap < 1 || V < 1 || R < 0) return SPEC_ERR_INVALID;
+  if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
+  if (B == 0) return SPEC_OK;
+  const size_t need = spec_verify_workspace_size(mode, B, T_cap, V, R);
+  if (need == 0) return SPEC_ERR_UNSUPPORTED;  // a vocabulary beyond the row merge
+  if (need > kNoAllocScratchBytes) return SPEC_ERR_CAPACITY;
+  void* ws = scratch_on_current_device();
+  if (!ws) return SPEC_ERR_HIP;
+  // no mode needs initial workspace contents: whatever the previous call on
+  // this device left in the array is overwritten before it is read
+  return spec_verify(mode, B, T_cap, V, R, tgt, dft, dft_row, n_nodes, parent, token, depth,
+                     u_node, u_final, acc_len, acc_path, next_token, p_tok, q_tok, decision,
+                     near_tie, ws, kNoAllocScratchBytes, status, stream);
 }
