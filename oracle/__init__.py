@@ -271,3 +271,31 @@ def kv_compact(k: np.ndarray, v: np.ndarray, ctx_len, acc_len, acc_path):
            _p(acc_path))
     _check(rc, "kv_compact")
     return ctx_len_io
+
+
+def resispec_proxy(p, q, x0: int, fill: int = 0, x0_mode: int = 0):
+    """The literal GetProxy steps for a rejected candidate x0: (r, k, Z)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    V = p.shape[0]
+    r = np.zeros(V, np.float64)
+    k = np.zeros(V, np.float64)
+    z = ctypes.c_double(0.0)
+    f = lib().orc_resispec_proxy
+    f.restype = ctypes.c_int
+    rc = f(V, _p(p), _p(q), int(x0), int(fill), int(x0_mode), _p(r), _p(k), ctypes.byref(z))
+    _check(rc, "resispec_proxy")
+    return r, k, z.value
+
+
+def multicand_marginal(p, q, n: int, shape: int = 0, fill: int = 0, x0_mode: int = 0):
+    """Output distribution of n i.i.d. candidates from q verified sequentially
+    (every path summed): shape 0 standard residuals, 1 the literal ResiSpec ones."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    out = np.zeros(p.shape[0], np.float64)
+    f = lib().orc_multicand_marginal
+    f.restype = ctypes.c_int
+    rc = f(p.shape[0], int(n), _p(p), _p(q), int(shape), int(fill), int(x0_mode), _p(out))
+    _check(rc, "multicand_marginal")
+    return out

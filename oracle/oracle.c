@@ -16,7 +16,9 @@
  *               Token Tree Construction and Tree Attention" (mask, Figure 4).
  *   [ResiSpec]  paperpeel 2608.24411 (residual drift in multi-candidate
  *               verification): section 4 (residual distribution, sequential
- *               verification of N candidates), Appendix B.1 (path marginals).
+ *               verification of N candidates), section 5 "Practical
+ *               Implementation" (GetProxy residual shaping, read literally in
+ *               part 7) and Appendix B.1 (path marginals).
  *
  * Conventions (readings where the pages are silent; each one is listed in the
  * design notes of the repository):
@@ -895,5 +897,152 @@ int orc_select_tree(int B, int N, int N_keep, const int32_t *cand_parent,
         }
     }
     free(S); free(ns); free(kept); free(newnode);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 7. Residual shaping (ResiSpec), literal reading, and path marginals       */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * GetProxy of [ResiSpec] section 5, "Practical Implementation: The ResiSpec
+ * Algorithm", taken step by step.  p is the current target, q the draft and x0
+ * the candidate just rejected (p(x0) < q(x0)).
+ *   Step 1 (budget and projection): Z = |q(x0) - p(x0)|; r(x) = min(Z q(x), p(x)).
+ *   Step 2 (capacity-aware redistribution): the deficit Z - sum r is moved onto
+ *     tokens with p > r, never past p, so that sum r = Z.
+ *   Step 3 (proxy): k = p - r, with k(x0) set to q(x0) (local alignment).
+ * The page leaves open how the water-filling spreads the deficit and whether x0
+ * takes part in Steps 1-2.  Readings:
+ *   fill 0: the draft shape is raised until the budget is met,
+ *           r(x) = min(lam Z q(x), p(x)) with the smallest lam >= 1 giving
+ *           sum r = Z (bisection on lam down to fp64 resolution);
+ *   fill 1: the deficit is spread in proportion to the remaining capacity
+ *           p(x) - r(x) (one step; no token passes p).
+ *   x0_mode 0: x0 is left out of Steps 1-2, r(x0) = 0.  This is the reading
+ *           under which k is a distribution: sum k = 1 + r(x0) in general.
+ *   x0_mode 1: x0 takes part in Steps 1-2 as written; k then sums to 1 + r(x0).
+ * The residual the next candidate is tested against is that of the test with
+ * the proxy, max(0, p - k) normalised: r off x0, 0 at x0 (p(x0) - q(x0) < 0).
+ * Outputs r [V] and k [V]; *z_out = Z.  Returns ORC_ERR for a bad argument or
+ * when q(x0) <= p(x0) (x0 cannot have been rejected).
+ */
+int orc_resispec_proxy(int V, const double *p, const double *q, int x0, int fill, int x0_mode,
+                       double *r, double *k, double *z_out)
+{
+    if (V < 1 || x0 < 0 || x0 >= V || (fill != 0 && fill != 1) ||
+        (x0_mode != 0 && x0_mode != 1))
+        return ORC_ERR;
+    if (!(q[x0] > p[x0])) return ORC_ERR;
+    const double Z = fabs(q[x0] - p[x0]);
+    /* Step 1 */
+    double sum = 0.0;
+    for (int v = 0; v < V; ++v) {
+        r[v] = (v == x0 && x0_mode == 0) ? 0.0 : fmin(Z * q[v], p[v]);
+        sum += r[v];
+    }
+    /* Step 2 */
+    if (sum < Z) {
+        if (fill == 0) {
+            double lo = 1.0, hi = 2.0;
+            for (;;) {
+                double s = 0.0;
+                for (int v = 0; v < V; ++v)
+                    if (!(v == x0 && x0_mode == 0)) s += fmin(hi * Z * q[v], p[v]);
+                if (s >= Z || hi > 1e300) break;
+                lo = hi;
+                hi *= 2.0;
+            }
+            for (int it = 0; it < 2000 && lo < hi; ++it) {
+                double mid = 0.5 * (lo + hi);
+                if (!(mid > lo && mid < hi)) break;
+                double s = 0.0;
+                for (int v = 0; v < V; ++v)
+                    if (!(v == x0 && x0_mode == 0)) s += fmin(mid * Z * q[v], p[v]);
+                if (s < Z) lo = mid;
+                else hi = mid;
+            }
+            for (int v = 0; v < V; ++v)
+                r[v] = (v == x0 && x0_mode == 0) ? 0.0 : fmin(hi * Z * q[v], p[v]);
+        } else {
+            double cap = 0.0;
+            for (int v = 0; v < V; ++v)
+                if (!(v == x0 && x0_mode == 0)) cap += p[v] - r[v];
+            const double deficit = Z - sum;
+            if (cap > 0.0)
+                for (int v = 0; v < V; ++v)
+                    if (!(v == x0 && x0_mode == 0)) r[v] += deficit * (p[v] - r[v]) / cap;
+        }
+    }
+    /* Step 3 */
+    for (int v = 0; v < V; ++v) k[v] = p[v] - r[v];
+    k[x0] = q[x0];
+    *z_out = Z;
+    return ORC_OK;
+}
+
+/* Path-marginal recursion: adds `weight` times the output distribution of the
+ * remaining n candidates, starting from target p, to out. */
+static int marginal_rec(int V, int n, const double *p, const double *q, int shape, int fill,
+                        int x0_mode, double weight, double *out, double *scratch)
+{
+    if (n == 0) {
+        for (int v = 0; v < V; ++v) out[v] += weight * p[v];
+        return ORC_OK;
+    }
+    double *pn = scratch;            /* the residual after rejecting x */
+    double *k = scratch + V;         /* the proxy (shape 1) */
+    double *deeper = scratch + 2 * V;
+    for (int x = 0; x < V; ++x) {
+        if (!(q[x] > 0.0)) continue;  /* never proposed */
+        const double a = p[x] >= q[x] ? 1.0 : p[x] / q[x];
+        out[x] += weight * q[x] * a;   /* x proposed and accepted */
+        if (a >= 1.0) continue;
+        const double w_rej = weight * q[x] * (1.0 - a);
+        double z = 0.0;
+        if (shape == 0) {
+            /* [ResiSpec] section 4: norm(max(0, p - q)) */
+            for (int v = 0; v < V; ++v) {
+                const double d = p[v] - q[v];
+                pn[v] = d > 0.0 ? d : 0.0;
+                z += pn[v];
+            }
+        } else {
+            double Z;
+            if (orc_resispec_proxy(V, p, q, x, fill, x0_mode, pn, k, &Z) != ORC_OK) return ORC_ERR;
+            for (int v = 0; v < V; ++v) {
+                const double d = p[v] - k[v];
+                pn[v] = d > 0.0 ? d : 0.0;
+                z += pn[v];
+            }
+        }
+        if (!(z > 0.0)) return ORC_ERR;
+        for (int v = 0; v < V; ++v) pn[v] /= z;
+        if (marginal_rec(V, n - 1, pn, q, shape, fill, x0_mode, w_rej, out, deeper) != ORC_OK)
+            return ORC_ERR;
+    }
+    return ORC_OK;
+}
+
+/*
+ * Output distribution of sequential verification of n candidates drawn i.i.d.
+ * from q, by summing every path ([ResiSpec] Appendix B.1): candidate i is
+ * accepted with probability min(1, p_{i-1}(x)/q(x)) against the current target
+ * p_{i-1} (p_0 = p); after a rejection the target becomes the next residual;
+ * after n rejections the token is drawn from p_n.  shape 0: the residual of
+ * section 4, norm(max(0, p - q)).  shape 1: the residual of the proxy test of
+ * section 5 (orc_resispec_proxy with `fill` and `x0_mode`); the test itself is
+ * unchanged, since k(x) = q(x) at the candidate.  Every path is enumerated:
+ * V^n of them (n <= 8).  out [V].
+ */
+int orc_multicand_marginal(int V, int n, const double *p, const double *q, int shape, int fill,
+                           int x0_mode, double *out)
+{
+    if (V < 1 || n < 0 || n > 8 || (shape != 0 && shape != 1)) return ORC_ERR;
+    double *scratch = (double *)malloc(sizeof(double) * (size_t)V * 2 * (size_t)(n + 1) + 8);
+    if (!scratch) return ORC_ERR;
+    for (int v = 0; v < V; ++v) out[v] = 0.0;
+    int rc = marginal_rec(V, n, p, q, shape, fill, x0_mode, 1.0, out, scratch);
+    free(scratch);
     return rc;
 }
