@@ -209,6 +209,40 @@ def verify_greedy_walk(tgt: np.ndarray, n_nodes, parent, token, depth):
     return out
 
 
+def verify_reject_walk(mode, tgt: np.ndarray, dft, dft_row, n_nodes, parent, token, depth, u_node,
+                       u_final):
+    """Rejection-mode verification walking the surviving nodes and reading only
+    their rows; see orc_verify_reject_walk in oracle.c.  Only tested nodes carry
+    decision / p_tok / q_tok; rows_tgt / rows_dft count the rows read."""
+    mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    tgt = np.ascontiguousarray(tgt, dtype=np.float32)
+    dft = np.ascontiguousarray(dft, dtype=np.float32)
+    B, T_cap, V = tgt.shape
+    out = dict(
+        acc_len=np.zeros(B, np.int32),
+        acc_path=np.zeros((B, T_cap), np.int32),
+        next_token=np.zeros(B, np.int32),
+        p_tok=np.zeros((B, T_cap), np.float64),
+        q_tok=np.zeros((B, T_cap), np.float64),
+        decision=np.zeros((B, T_cap), np.int8),
+        near_tie=np.zeros(B, np.int32),
+        fallback=np.zeros(B, np.int32),
+        rows_tgt=np.zeros(B, np.int32),
+        rows_dft=np.zeros(B, np.int32),
+    )
+    f = lib().orc_verify_reject_walk
+    f.restype = ctypes.c_int
+    rc = f(mode, B, T_cap, V, dft.shape[1], _p(tgt), _p(dft), _p(_i32(dft_row)),
+           _p(_i32(n_nodes)), _p(_i32(parent)), _p(_i32(token)), _p(_i32(depth)),
+           _p(np.ascontiguousarray(u_node, dtype=np.float32)),
+           _p(np.ascontiguousarray(u_final, dtype=np.float32)),
+           _p(out["acc_len"]), _p(out["acc_path"]), _p(out["next_token"]), _p(out["p_tok"]),
+           _p(out["q_tok"]), _p(out["decision"]), _p(out["near_tie"]), _p(out["fallback"]),
+           _p(out["rows_tgt"]), _p(out["rows_dft"]))
+    _check(rc, "verify_reject_walk")
+    return out
+
+
 def beam_topk(logp: np.ndarray, beam_score, K_out: int, hist=None):
     """One beam-search pruning step; see orc_beam_topk in oracle.c.
     logp [B][K_in][V] fp32, beam_score [B][K_in] or None, hist [B][K_in][len] or None."""

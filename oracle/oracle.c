@@ -658,6 +658,199 @@ int orc_verify_greedy_walk(int B, int T_cap, int V, const float *tgt, const int3
 }
 
 /*
+ * Rejection-mode verification by walking the tree from the root, reading only
+ * the rows the decisions need ([ReDrafter] "The Full Speculative Decoding
+ * Loop", Step 5, rejection sampling; [ResiSpec] section 4, sequential
+ * verification).  The acceptance, stop node and next token are those of
+ * orc_verify in the same mode; what changes is which rows are read.
+ *
+ * ORC_REJECT_PATH: the nodes whose whole path is accepted are explored depth by
+ *   depth.  The frontier starts as {root}; for every frontier node f with
+ *   children, f's target row and draft row give p_f and q_f, and each child c
+ *   (token x) is accepted iff u_node[c] < p_f(x) / q_f(x).  The accepted
+ *   children form the next frontier.  The stop node s is the lowest-index node
+ *   of the deepest non-empty frontier.  The next token is drawn with u_final
+ *   from norm(max(0, p_s - q_s)) if s has children (all rejected), else from
+ *   p_s, whose target row is read then.
+ * ORC_REJECT_RECURSIVE: the walk of orc_verify, reading the target and draft
+ *   rows of each node it moves to (when it has children) and, at a stop node
+ *   without children, that node's target row.
+ *
+ * Outputs as orc_verify, except that only tested nodes (children of nodes
+ * whose rows were read) get decision, p_tok and q_tok; all other entries are
+ * -1, 0 and 0, and near_tie counts the tested nodes' near-ties (plus a CDF
+ * near-tie).  rows_tgt[b] and rows_dft[b] count the target and draft rows read
+ * (a row read twice is counted twice).
+ */
+int orc_verify_reject_walk(int mode, int B, int T_cap, int V, int R, const float *tgt,
+                           const float *dft, const int32_t *dft_row, const int32_t *n_nodes,
+                           const int32_t *parent, const int32_t *token, const int32_t *depth,
+                           const float *u_node, const float *u_final, int32_t *acc_len,
+                           int32_t *acc_path, int32_t *next_token, double *p_tok, double *q_tok,
+                           int8_t *decision, int32_t *near_tie, int32_t *fallback,
+                           int32_t *rows_tgt, int32_t *rows_dft)
+{
+    if (mode != ORC_REJECT_PATH && mode != ORC_REJECT_RECURSIVE) return ORC_ERR;
+    if (B < 0 || T_cap < 1 || V < 1 || !dft || !dft_row || R < 1) return ORC_ERR;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    double *r = (double *)malloc(sizeof(double) * (size_t)V);
+    int *front = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *next = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    int *n_child = (int *)malloc(sizeof(int) * (size_t)T_cap);
+    if (!p || !q || !r || !front || !next || !n_child) {
+        free(p); free(q); free(r); free(front); free(next); free(n_child);
+        return ORC_ERR;
+    }
+    int rc = ORC_OK;
+    for (int b = 0; b < B && rc == ORC_OK; ++b) {
+        const int T = n_nodes[b];
+        const int32_t *par = parent + (size_t)b * T_cap;
+        const int32_t *tok = token + (size_t)b * T_cap;
+        const int32_t *dep = depth + (size_t)b * T_cap;
+        const int32_t *drow = dft_row + (size_t)b * T_cap;
+        const float *ub = u_node + (size_t)b * T_cap;
+        int32_t *path = acc_path + (size_t)b * T_cap;
+        int8_t *dec = decision + (size_t)b * T_cap;
+        double *pt = p_tok + (size_t)b * T_cap;
+        double *qt = q_tok + (size_t)b * T_cap;
+        if (T < 1 || T > T_cap) { rc = ORC_ERR; break; }
+        for (int t = 0; t < T_cap; ++t) {
+            path[t] = -1;
+            dec[t] = -1;
+            pt[t] = 0.0;
+            qt[t] = 0.0;
+            n_child[t] = 0;
+        }
+        for (int t = 1; t < T; ++t) {
+            if (par[t] < 0 || par[t] >= t || tok[t] < 0 || tok[t] >= V) { rc = ORC_ERR; break; }
+            n_child[par[t]]++;
+        }
+        for (int t = 0; t < T && rc == ORC_OK; ++t)
+            if (n_child[t] > 0 && (drow[t] < 0 || drow[t] >= R)) rc = ORC_ERR;
+        if (rc != ORC_OK) break;
+        near_tie[b] = 0;
+        fallback[b] = 0;
+        int n_tgt = 0, n_dft = 0;
+        const float *tgt_b = tgt + (size_t)b * T_cap * V;
+        const float *dft_b = dft + (size_t)b * R * V;
+        int stop = 0;
+        int rows_of = -1;   /* node whose p (and q) are in p / q */
+        int draw_resid = 0; /* draw from the residual (1) or from p_stop (0) */
+
+        if (mode == ORC_REJECT_PATH) {
+            int n_front = 1;
+            front[0] = 0;
+            while (n_front > 0) {
+                stop = front[0];
+                int n_next = 0;
+                for (int i = 0; i < n_front; ++i) {
+                    const int f = front[i];
+                    if (n_child[f] == 0) continue;
+                    softmax_row(V, tgt_b + (size_t)f * V, p);
+                    softmax_row(V, dft_b + (size_t)drow[f] * V, q);
+                    ++n_tgt;
+                    ++n_dft;
+                    rows_of = f;
+                    for (int c = f + 1; c < T; ++c) {
+                        if (par[c] != f) continue;
+                        const int x = tok[c];
+                        pt[c] = p[x];
+                        qt[c] = q[x];
+                        const double ratio = q[x] > 0.0 ? p[x] / q[x] : (p[x] > 0.0 ? INFINITY : 0.0);
+                        const double u = (double)ub[c];
+                        if (fabs(ratio - u) < ORC_NEAR_TIE) near_tie[b]++;
+                        dec[c] = (int8_t)(u < ratio);
+                        if (dec[c]) next[n_next++] = c;
+                    }
+                }
+                for (int i = 1; i < n_next; ++i)
+                    for (int j = i; j > 0 && next[j - 1] > next[j]; --j) {
+                        const int x = next[j]; next[j] = next[j - 1]; next[j - 1] = x;
+                    }
+                memcpy(front, next, sizeof(int) * (size_t)n_next);
+                n_front = n_next;
+            }
+            if (n_child[stop] > 0) {
+                /* the stop node's rows were read when it was on the frontier */
+                if (rows_of != stop) {
+                    softmax_row(V, tgt_b + (size_t)stop * V, p);
+                    softmax_row(V, dft_b + (size_t)drow[stop] * V, q);
+                    ++n_tgt;
+                    ++n_dft;
+                }
+                memcpy(r, p, sizeof(double) * (size_t)V);
+                if (residual_step(V, r, q) > 0.0) {
+                    draw_resid = 1;
+                } else {
+                    fallback[b] = 1;
+                }
+            }
+        } else {
+            int s = 0;
+            for (;;) {
+                int moved = 0, dead = 0, rejected = 0;
+                if (n_child[s] > 0) {
+                    softmax_row(V, tgt_b + (size_t)s * V, p);
+                    softmax_row(V, dft_b + (size_t)drow[s] * V, q);
+                    ++n_tgt;
+                    ++n_dft;
+                    rows_of = s;
+                    memcpy(r, p, sizeof(double) * (size_t)V);
+                    for (int c = s + 1; c < T; ++c) {
+                        if (par[c] != s) continue;
+                        const int x = tok[c];
+                        pt[c] = p[x];
+                        qt[c] = q[x];
+                        if (dead) {
+                            dec[c] = 0;
+                            continue;
+                        }
+                        const double ratio = q[x] > 0.0 ? r[x] / q[x] : (r[x] > 0.0 ? INFINITY : 0.0);
+                        const double u = (double)ub[c];
+                        if (fabs(ratio - u) < ORC_NEAR_TIE) near_tie[b]++;
+                        if (u < ratio) {
+                            dec[c] = 1;
+                            s = c;
+                            moved = 1;
+                            break;
+                        }
+                        dec[c] = 0;
+                        rejected = 1;
+                        if (!(residual_step(V, r, q) > 0.0)) {
+                            dead = 1;
+                            fallback[b] = 1;
+                        }
+                    }
+                }
+                if (moved) continue;
+                stop = s;
+                draw_resid = rejected && !dead;
+                break;
+            }
+        }
+
+        acc_len[b] = dep[stop];
+        for (int cur = stop; cur >= 0; cur = par[cur]) path[dep[cur]] = cur;
+        if (!draw_resid) {
+            /* p_stop: a leaf's (or a fallback's) target row */
+            if (rows_of != stop) {
+                softmax_row(V, tgt_b + (size_t)stop * V, p);
+                ++n_tgt;
+            }
+            memcpy(r, p, sizeof(double) * (size_t)V);
+        }
+        int near = 0;
+        next_token[b] = sample_inverse_cdf(V, r, (double)u_final[b], &near);
+        near_tie[b] += near;
+        rows_tgt[b] = n_tgt;
+        rows_dft[b] = n_dft;
+    }
+    free(p); free(q); free(r); free(front); free(next); free(n_child);
+    return rc;
+}
+
+/*
  * Residual chain of one (p, q) pair, for pins of the closed form.
  * literal = 0: closed form, c_0 = 0, Z_0 = 1, c_{k+1} = c_k + Z_k,
  *   Z_{k+1} = sum max(0, p - c_{k+1} q); dist_k = max(0, p - c_k q) / Z_k.
