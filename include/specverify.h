@@ -79,7 +79,9 @@ typedef enum {
     SPEC_GREEDY = 0,
     SPEC_REJECT_PATH = 1,
     SPEC_REJECT_RECURSIVE = 2,
-    SPEC_GREEDY_WALK = 3
+    SPEC_GREEDY_WALK = 3,
+    SPEC_REJECT_PATH_WALK = 4,
+    SPEC_REJECT_RECURSIVE_WALK = 5
 } spec_verify_mode;
 
 /* Library version as 10000*major + 100*minor + patch (host only). */

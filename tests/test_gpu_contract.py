@@ -101,16 +101,22 @@ def test_compact_long_paths(gpu, Hkv, D, dtype):
     assert int(status.item()) == 0x8  # the refused path of sequence 4
 
 
-@pytest.mark.parametrize("mode", ["greedy_walk", "reject_recursive", "greedy"])
+@pytest.mark.parametrize("mode", ["greedy_walk", "reject_recursive", "greedy", "reject_path_walk",
+                                  "reject_recursive_walk"])
 def test_verify_on_a_workspace_of_arbitrary_bytes(gpu, mode):
     """No initial workspace contents are needed: the workspace is filled with
     random bytes (and, for the walk, with words that carry plausible tags of
     other calls) before each of two calls on two input sets."""
     sets = []
     for seed in (312, 313):
-        inp = synth.make_inputs(1, seed) if mode != "reject_recursive" else \
+        inp = synth.make_inputs(1, seed) if "recursive" not in mode else \
             synth.make_inputs(4, seed, B_override=2, ctx_override=100)
-        sets.append((inp, oracle_verify(inp, oracle_tree(inp), mode)))
+        tr = oracle_tree(inp)
+        ref = oracle_verify(inp, tr, mode) if "walk" not in mode or mode == "greedy_walk" else \
+            oracle.verify_reject_walk(mode.replace("_walk", ""), inp["tgt"], inp["dft"],
+                                      inp["dft_row"], tr["n_nodes"], tr["parent"], tr["token"],
+                                      tr["depth"], inp["u_node"], inp["u_final"])
+        sets.append((inp, ref))
     steps = [pipeline.Step(inp, mode, with_kv=False) for inp, _ in sets]
     ws = steps[0].ver_ws
     steps[1].ver_ws, steps[1].ver_ws_bytes = ws, steps[0].ver_ws_bytes

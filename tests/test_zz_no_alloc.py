@@ -20,6 +20,9 @@ CASES = {
     "greedy_walk": ((2, dict(ctx_override=64)), (1, dict(ctx_override=64))),
     "reject_path": ((3, dict(B_override=16, ctx_override=64)), (0, {})),
     "reject_recursive": ((4, dict(ctx_override=64)), (4, dict(B_override=1, ctx_override=64))),
+    "reject_path_walk": ((3, dict(B_override=16, ctx_override=64)), (0, {})),
+    "reject_recursive_walk": ((4, dict(ctx_override=64)),
+                              (4, dict(B_override=1, ctx_override=64))),
 }
 
 

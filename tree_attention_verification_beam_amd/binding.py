@@ -16,8 +16,11 @@ LIB_PATH = _PKG / "libspecverify.so"
 SPEC_F32, SPEC_BF16 = 0, 1
 SPEC_TREE_BEAMS, SPEC_TREE_EXPLICIT = 0, 1
 SPEC_GREEDY, SPEC_REJECT_PATH, SPEC_REJECT_RECURSIVE, SPEC_GREEDY_WALK = 0, 1, 2, 3
+SPEC_REJECT_PATH_WALK, SPEC_REJECT_RECURSIVE_WALK = 4, 5
 MODES = {"greedy": SPEC_GREEDY, "reject_path": SPEC_REJECT_PATH,
-         "reject_recursive": SPEC_REJECT_RECURSIVE, "greedy_walk": SPEC_GREEDY_WALK}
+         "reject_recursive": SPEC_REJECT_RECURSIVE, "greedy_walk": SPEC_GREEDY_WALK,
+         "reject_path_walk": SPEC_REJECT_PATH_WALK,
+         "reject_recursive_walk": SPEC_REJECT_RECURSIVE_WALK}
 
 DEV_BITS = {
     0x1: "BAD_PARENT", 0x2: "BAD_TOKEN", 0x4: "BAD_ROW", 0x8: "CTX_RANGE",

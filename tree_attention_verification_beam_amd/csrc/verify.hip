@@ -26,6 +26,7 @@
 //             then holds the same totals and takes the same decisions.  The
 //             grid is sized to be resident at once (occupancy query) and every
 //             wait is bounded.
+#include <atomic>
 #include <mutex>
 
 #include "common.hpp"
@@ -49,6 +50,15 @@ constexpr int kMaxP = 32;
 constexpr int kMergeEntries = 1024;  // chunk partials staged in LDS per merge batch
 constexpr int kSyncWords = 2 * kMaxP * 4;  // [2 parities][kMaxP][4 tagged halves]
 constexpr size_t kSyncStride = kSyncWords * 8;  // bytes of sync area per sequence
+// rejection-mode walks: rows scanned per exchange (target and draft rows of up
+// to kScanRows / 2 frontier nodes), 4 tagged 32-bit words per row
+constexpr int kScanRows = 8;
+constexpr int kXWords = 4 * kScanRows;
+// Per sequence the walks keep [2 parities][Pb][4] words for exchange() and
+// [2 parities][Pb][kXWords] for exchange_words(), Pb = the most workgroups a
+// sequence can get at this vocabulary size
+__host__ __device__ inline int walk_p_bound(int V) { return V / 2048 < 1 ? 1 : (V / 2048 > kMaxP ? kMaxP : V / 2048); }
+__host__ __device__ inline size_t walk_stride(int V) { return (size_t)walk_p_bound(V) * (2 * 4 + 2 * kXWords) * 8; }
 constexpr double kNearTie = 1e-5;
 constexpr double kCdfNearTie = 1e-9;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -93,7 +103,7 @@ VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
 
 // ------------------------------------------------------------------ block reductions
 
-__device__ double block_sum_f64(double v, double* s_red) {
+__device__ __forceinline__ double block_sum_f64(double v, double* s_red) {
   v = wave_sum_f64(v);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   __syncthreads();
@@ -105,7 +115,7 @@ __device__ double block_sum_f64(double v, double* s_red) {
 }
 
 // two sums at once
-__device__ void block_sum2_f64(double& a, double& b, double* s_red) {
+__device__ __forceinline__ void block_sum2_f64(double& a, double& b, double* s_red) {
   a = wave_sum_f64(a);
   b = wave_sum_f64(b);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -125,7 +135,7 @@ __device__ void block_sum2_f64(double& a, double& b, double* s_red) {
 }
 
 // exclusive scan over the block's threads (in thread order), fp64; returns the total
-__device__ double block_exclusive_scan_f64(double v, double* s_buf, double& excl) {
+__device__ __forceinline__ double block_exclusive_scan_f64(double v, double* s_buf, double& excl) {
   const int tid = threadIdx.x;
   __syncthreads();
   s_buf[tid] = v;
@@ -255,6 +265,8 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
 
 struct SelArgs {
   int B, T_cap, V, Rr, n_chunks, P, cache;
+  int slice;           // walks: vocabulary entries per workgroup (a multiple of 4)
+  uint32_t tag_base;   // walks: this call's exchange-tag base (bits 12..31), never 0
   const float* tgt;
   const float* dft;
   const int32_t* dft_row;
@@ -303,13 +315,70 @@ struct SelShared {
   int n_jobs;
   int near_count;
   int stop;
+  // rejection-mode walks: frontier, scan list, per-workgroup row statistics
+  // and the word exchange
+  int front[SPEC_MAX_TREE];
+  int scan_node[SPEC_MAX_TREE];
+  int in_batch[SPEC_MAX_TREE];
+  int n_front, n_scan;
+  float sc_m[kScanRows];
+  int sc_a[kScanRows];
+  double sc_S[kScanRows];
+  float wm[kSelWaves];
+  int wa[kSelWaves];
+  double wsum[kSelWaves];
+  uint32_t xw_mine[kXWords];
+  uint32_t xw_all[kMaxP * kXWords];
 };
 
 // Cross-workgroup meeting point of the P workgroups of one sequence.
 struct SeqSync {
-  uint64_t* slot;  // [2 parities][kMaxP][4]: low/high halves of a, then of b
+  uint64_t* slot;   // [2 parities][kMaxP][4]: low/high halves of a, then of b
+  uint64_t* wslot;  // [2 parities][kMaxP][kXWords] (the walks' word exchange)
   int P, w, rounds;
+  int pmax;           // workgroup capacity of the slot areas (>= P)
+  uint32_t tag_base;  // 0 when the slots are cleared before the call, else a per-call epoch
   int32_t* status;
+
+  // Everyone publishes nw (<= kXWords) 32-bit words, waits for the other
+  // workgroups and returns all P x nw words in `all` ([P][nw], identical in
+  // every workgroup).  Tags and parities as in exchange() below.
+  __device__ __forceinline__ void exchange_words(const uint32_t* mine, int nw, uint32_t* all) {
+    if (P == 1) {
+      for (int i = threadIdx.x; i < nw; i += kSelThreads) all[i] = mine[i];
+      __syncthreads();
+      ++rounds;
+      return;
+    }
+    __syncthreads();
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const uint32_t tag = tag_base + (uint32_t)rounds + 1u;
+      uint64_t* base = wslot + (size_t)(rounds & 1) * pmax * kXWords;
+      for (int i = lane; i < nw; i += 64)
+        store_coherent(base + (size_t)w * kXWords + i, ((uint64_t)tag << 32) | mine[i]);
+      // every workgroup's words, lane-strided
+      const int n = P * kXWords;
+      int spins = 0;
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const int wi = i / kXWords, k = i - wi * kXWords;
+        bool ok = i >= n || k >= nw;
+        uint64_t v = 0;
+        while (!ok) {
+          v = load_coherent(base + i);
+          ok = (uint32_t)(v >> 32) == tag;
+          if (!ok && ++spins > (1 << 22)) {
+            raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
+            break;
+          }
+        }
+        if (i < n && k < nw) all[wi * nw + k] = (uint32_t)v;
+      }
+    }
+    __syncthreads();
+    ++rounds;
+  }
 
   // Everyone publishes (a, b), waits for the other workgroups and returns the
   // per-workgroup values in s_slots (identical in every workgroup).  Word k of
@@ -318,7 +387,7 @@ struct SeqSync {
   // with the current tag is this round's, whatever order the stores landed in.
   // Round r + 2 reuses round r's parity only after every workgroup has
   // published round r + 1, i.e. after every reader is done with round r.
-  __device__ void exchange(double a, double b, double* s_slots) {
+  __device__ __forceinline__ void exchange(double a, double b, double* s_slots) {
     if (P == 1) {
       if (threadIdx.x == 0) {
         s_slots[0] = a;
@@ -331,8 +400,8 @@ struct SeqSync {
     __syncthreads();
     if (threadIdx.x < 64) {
       const int lane = threadIdx.x;
-      const uint32_t tag = (uint32_t)rounds + 1u;
-      uint64_t* base = slot + (size_t)(rounds & 1) * kMaxP * 4;
+      const uint32_t tag = tag_base + (uint32_t)rounds + 1u;
+      uint64_t* base = slot + (size_t)(rounds & 1) * pmax * 4;
       if (lane < 4) {
         const uint64_t bits = (uint64_t)__double_as_longlong(lane < 2 ? a : b);
         const uint32_t half = (lane & 1) ? (uint32_t)(bits >> 32) : (uint32_t)bits;
@@ -407,7 +476,7 @@ __device__ inline Slice slice_of(int V, int P, int w) {
 }
 
 // Accurate softmax normalisers of a row pair: sum exp(l - m) in fp64 over V.
-__device__ void pass_normalisers(RowPair& rp, bool with_q, SeqSync& sy, SelShared& sh, int V) {
+__device__ __forceinline__ void pass_normalisers(RowPair& rp, bool with_q, SeqSync& sy, SelShared& sh, int V) {
   const Slice sl = slice_of(V, sy.P, sy.w);
   double a = 0.0, b = 0.0;
   for (int v = sl.lo + threadIdx.x; v < sl.hi; v += kSelThreads) {
@@ -427,7 +496,7 @@ __device__ void pass_normalisers(RowPair& rp, bool with_q, SeqSync& sy, SelShare
 }
 
 // Normaliser of the next residual: sum_v max(0, r_k(v) - q(v)).
-__device__ double pass_residual_mass(const RowPair& rp, int k, const double* invN, SeqSync& sy,
+__device__ __forceinline__ double pass_residual_mass(const RowPair& rp, int k, const double* invN, SeqSync& sy,
                                      SelShared& sh, int V) {
   const Slice sl = slice_of(V, sy.P, sy.w);
   double a = 0.0;
@@ -449,7 +518,7 @@ __device__ double pass_residual_mass(const RowPair& rp, int k, const double* inv
 // Each thread owns a contiguous range of its workgroup's slice.  Returns true in
 // the one workgroup that found the token (written to *out_tok / *out_near);
 // *total_out gets the total weight (all workgroups).
-__device__ bool pass_draw(const RowPair& rp, int k, const double* invN, double u, SeqSync& sy,
+__device__ __forceinline__ bool pass_draw(const RowPair& rp, int k, const double* invN, double u, SeqSync& sy,
                           SelShared& sh, int V, int* out_tok, int* out_near, double* total_out) {
   const Slice sl = slice_of(V, sy.P, sy.w);
   const int n = sl.hi - sl.lo;
@@ -565,7 +634,7 @@ __device__ inline void cache_range(RowCache& c, int V, const SeqSync& sy) {
 
 // exp(l - m) of the row pair (q side only when with_q); with `normalise` the
 // fp64 totals are exchanged and both sides become p and q
-__device__ void cache_load(RowCache& c, RowPair& rp, bool with_q, bool normalise, SeqSync& sy,
+__device__ __forceinline__ void cache_load(RowCache& c, RowPair& rp, bool with_q, bool normalise, SeqSync& sy,
                            SelShared& sh) {
   double a = 0.0, bq = 0.0;
 #pragma unroll
@@ -600,7 +669,7 @@ __device__ void cache_load(RowCache& c, RowPair& rp, bool with_q, bool normalise
 }
 
 // sum over the vocabulary of max(0, r - q), the next residual's normaliser
-__device__ double cache_residual_mass(const RowCache& c, SeqSync& sy, SelShared& sh) {
+__device__ __forceinline__ double cache_residual_mass(const RowCache& c, SeqSync& sy, SelShared& sh) {
   double a = 0.0;
 #pragma unroll
   for (int e = 0; e < kCacheE; ++e) {
@@ -632,7 +701,7 @@ __device__ inline double cache_weight(const RowCache& c, int e, bool resid) {
 
 // The inverse-CDF draw of pass_draw over cached weights: r itself (resid ==
 // false) or max(0, r - q).
-__device__ bool cache_draw(const RowCache& c, bool resid, double u, SeqSync& sy, SelShared& sh,
+__device__ __forceinline__ bool cache_draw(const RowCache& c, bool resid, double u, SeqSync& sy, SelShared& sh,
                            int V, int* out_tok, int* out_near, double* total_out) {
   const Slice sl = slice_of(V, sy.P, sy.w);
   double mine = 0.0;
@@ -721,6 +790,131 @@ __device__ bool cache_draw(const RowCache& c, bool resid, double u, SeqSync& sy,
   return true;
 }
 
+// Sequential checking of the children of node s ([ResiSpec] section 4): in
+// node-index order against the running target p' (p_s at first), p' <-
+// norm(max(0, p' - q_s)) after each rejection.  sh.pt / sh.qt of the children
+// and the statistics of s's rows must be in place.  Returns true (and the
+// child in next_s) on an acceptance; otherwise the draw description for s:
+// draw_k (-1: from p_s) and whether rc holds the row pair.
+__device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, int s, int T, RowPair& rp,
+                                  RowCache& rc, SeqSync& sy, SelShared& sh, int& draw_k,
+                                  bool& cached, int& next_s) {
+  const int tid = threadIdx.x;
+  const int V = A.V;
+  const int b = (int)(nb / A.T_cap);
+  const double* invN = sh.invN;
+  int k = 0;
+  draw_k = -1;
+  cached = false;
+  bool dead = false, have_norm = false, moved = false;
+  rp.lp = A.tgt + (nb + s) * V;
+  rp.mp = sh.m_p[s];
+  if (sh.nch[s] > 0) {
+    const int r = sh.row[s];
+    rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
+    rp.mq = sh.m_q[s];
+  }
+  int remaining = sh.nch[s];
+  for (int ch = s + 1; ch < T && remaining > 0; ++ch) {
+    if (sh.par[ch] != s) continue;
+    --remaining;
+    if (dead) {
+      if (tid == 0) sh.dec[ch] = 0;
+      continue;
+    }
+    const int x = sh.tok[ch];
+    double ratio;
+    if (k == 0) {
+      const double p = sh.pt[ch], q = sh.qt[ch];
+      ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
+    } else {
+      double qv;
+      const double r = eval_r(rp, x, k, invN, qv);
+      ratio = qv > 0.0 ? r / qv : (r > 0.0 ? INFINITY : 0.0);
+    }
+    const double u = (double)A.u_node[nb + ch];
+    if (tid == 0 && fabs(ratio - u) < kNearTie) sh.near_count++;
+    if (u < ratio) {
+      if (tid == 0) sh.dec[ch] = 1;
+      next_s = ch;
+      moved = true;
+      break;
+    }
+    if (tid == 0) sh.dec[ch] = 0;
+    if (!have_norm) {
+      if (A.cache) {
+        cache_load(rc, rp, true, true, sy, sh);
+        cached = true;
+      } else {
+        pass_normalisers(rp, true, sy, sh, V);
+      }
+      have_norm = true;
+    }
+    if (remaining == 0) {
+      // last child rejected: the draw uses max(0, r_k - q) unnormalised
+      draw_k = k;
+      break;
+    }
+    const double N =
+        A.cache ? cache_residual_mass(rc, sy, sh) : pass_residual_mass(rp, k, invN, sy, sh, V);
+    if (!(N > 0.0) || k >= 63) {
+      dead = true;
+      if (tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
+    } else {
+      if (tid == 0) sh.invN[k] = 1.0 / N;
+      if (A.cache) cache_residual_step(rc, 1.0 / N);
+      __syncthreads();
+      ++k;
+    }
+  }
+  __syncthreads();
+  if (moved) return true;
+  if (dead) draw_k = -1;
+  return false;
+}
+
+// The next token at the stop node: its greedy token (greedy mode, or a bad
+// sequence), else an inverse-CDF draw with u_final from the residual after
+// draw_k rejections (draw_k >= 0; with `cached` the row pair sits in rc) or
+// from p_stop (draw_k < 0).  rp.lp, rp.mp (and the q side for draw_k >= 0)
+// describe the stop rows.  Returns true in the workgroup that holds the token.
+__device__ __forceinline__ bool final_token(bool greedy, const SelArgs& A, size_t nb, int stop, bool bad,
+                            int draw_k, bool cached, RowPair& rp, RowCache& rc, SeqSync& sy,
+                            SelShared& sh, bool lead, int& next, int& cdf_near) {
+  const int tid = threadIdx.x;
+  const int V = A.V;
+  const double* invN = sh.invN;
+  const int b = (int)(nb / A.T_cap);
+  if (greedy || bad) {
+    next = sh.arg_p[stop];
+    return lead;
+  }
+  rp.lp = A.tgt + (nb + stop) * V;
+  rp.mp = sh.m_p[stop];
+  const double u = (double)A.u_final[b];
+  double total = 0.0;
+  int tok = 0, near = 0;
+  bool found;
+  if (A.cache && draw_k >= 0 && cached) {
+    found = cache_draw(rc, true, u, sy, sh, V, &tok, &near, &total);
+  } else if (A.cache && draw_k < 0) {
+    cache_load(rc, rp, false, false, sy, sh);
+    found = cache_draw(rc, false, u, sy, sh, V, &tok, &near, &total);
+  } else {
+    found = pass_draw(rp, draw_k, invN, u, sy, sh, V, &tok, &near, &total);
+  }
+  if (!(total > 0.0) && draw_k >= 0) {
+    // nothing left in the residual (rounding only): draw from p_stop
+    if (lead && tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
+    found = pass_draw(rp, -1, invN, u, sy, sh, V, &tok, &near, &total);
+  }
+  if (found) {
+    next = tok;
+    cdf_near = near;
+  }
+  return found;
+}
+
 template <int MODE>
 __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   __shared__ SelShared sh;
@@ -733,6 +927,9 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   sy.P = A.P;
   sy.w = w;
   sy.rounds = 0;
+  sy.pmax = kMaxP;
+  sy.tag_base = 0;  // k_vstats cleared the slots
+  sy.wslot = nullptr;
   sy.status = A.status;
   const bool lead = w == 0;
 
@@ -888,7 +1085,6 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   int stop = 0;
   // draw description for the final token
   int draw_k = -1;          // -1: draw from p_stop; k >= 0: from max(0, r_k - q)
-  const double* invN = sh.invN;
   RowPair rp{};
   RowCache rc;
   bool cached = false;  // rc holds the current node's normalised pair (residual after k steps)
@@ -943,111 +1139,20 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     // sequential multi-candidate verification with residual renormalisation
     int s = 0;
     for (;;) {
-      int k = 0;
-      draw_k = -1;
-      cached = false;
-      bool dead = false, have_norm = false, moved = false;
-      rp.lp = A.tgt + (nb + s) * V;
-      rp.mp = sh.m_p[s];
-      if (sh.nch[s] > 0) {
-        const int r = sh.row[s];
-        rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
-        rp.mq = sh.m_q[s];
+      int next_s = s;
+      if (test_children_seq(A, nb, s, T, rp, rc, sy, sh, draw_k, cached, next_s)) {
+        s = next_s;
+        continue;
       }
-      int remaining = sh.nch[s];
-      for (int ch = s + 1; ch < T && remaining > 0; ++ch) {
-        if (sh.par[ch] != s) continue;
-        --remaining;
-        if (dead) {
-          if (tid == 0) sh.dec[ch] = 0;
-          continue;
-        }
-        const int x = sh.tok[ch];
-        double ratio;
-        if (k == 0) {
-          const double p = sh.pt[ch], q = sh.qt[ch];
-          ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
-        } else {
-          double qv;
-          const double r = eval_r(rp, x, k, invN, qv);
-          ratio = qv > 0.0 ? r / qv : (r > 0.0 ? INFINITY : 0.0);
-        }
-        const double u = (double)A.u_node[nb + ch];
-        if (tid == 0 && fabs(ratio - u) < kNearTie) sh.near_count++;
-        if (u < ratio) {
-          if (tid == 0) sh.dec[ch] = 1;
-          s = ch;
-          moved = true;
-          break;
-        }
-        if (tid == 0) sh.dec[ch] = 0;
-        if (!have_norm) {
-          if (A.cache) {
-            cache_load(rc, rp, true, true, sy, sh);
-            cached = true;
-          } else {
-            pass_normalisers(rp, true, sy, sh, V);
-          }
-          have_norm = true;
-        }
-        if (remaining == 0) {
-          // last child rejected: the draw uses max(0, r_k - q) unnormalised
-          draw_k = k;
-          break;
-        }
-        const double N =
-            A.cache ? cache_residual_mass(rc, sy, sh) : pass_residual_mass(rp, k, invN, sy, sh, V);
-        if (!(N > 0.0) || k >= 63) {
-          dead = true;
-          if (tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
-        } else {
-          if (tid == 0) sh.invN[k] = 1.0 / N;
-          if (A.cache) cache_residual_step(rc, 1.0 / N);
-          __syncthreads();
-          ++k;
-        }
-      }
-      __syncthreads();
-      if (moved) continue;
       stop = s;
-      if (dead) draw_k = -1;
       break;
     }
   }
 
   // ---------------------------------------------------------------- final token
-  int next = 0;
-  bool have_next = false;
-  int cdf_near = 0;
-  if (MODE == SPEC_GREEDY || bad) {
-    next = sh.arg_p[stop];
-    have_next = lead;
-  } else {
-    rp.lp = A.tgt + (nb + stop) * V;
-    rp.mp = sh.m_p[stop];
-    const double u = (double)A.u_final[b];
-    double total = 0.0;
-    int tok = 0, near = 0;
-    bool found;
-    if (A.cache && draw_k >= 0 && cached) {
-      found = cache_draw(rc, true, u, sy, sh, V, &tok, &near, &total);
-    } else if (A.cache && draw_k < 0) {
-      cache_load(rc, rp, false, false, sy, sh);
-      found = cache_draw(rc, false, u, sy, sh, V, &tok, &near, &total);
-    } else {
-      found = pass_draw(rp, draw_k, invN, u, sy, sh, V, &tok, &near, &total);
-    }
-    if (!(total > 0.0) && draw_k >= 0) {
-      // nothing left in the residual (rounding only): draw from p_stop
-      if (lead && tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
-      found = pass_draw(rp, -1, invN, u, sy, sh, V, &tok, &near, &total);
-    }
-    if (found) {
-      next = tok;
-      cdf_near = near;
-      have_next = true;
-    }
-  }
+  int next = 0, cdf_near = 0;
+  const bool have_next = final_token(MODE == SPEC_GREEDY, A, nb, stop, bad, draw_k, cached, rp,
+                                     rc, sy, sh, lead, next, cdf_near);
 
   // ---------------------------------------------------------------- outputs
   const int near_total = sh.near_count + cdf_near;
@@ -1069,6 +1174,440 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     if (A.decision) A.decision[nb + t] = (int8_t)((t < T && !bad) ? sh.dec[t] : -1);
     if (A.p_tok) A.p_tok[nb + t] = (t < T && !bad) ? (float)sh.pt[t] : 0.0f;
     if (A.q_tok) A.q_tok[nb + t] = (t < T && !bad) ? (float)sh.qt[t] : 0.0f;
+  }
+}
+
+
+// ------------------------------------------------------------------ rejection-mode walks
+// Rejection sampling that reads only the rows the decisions need
+// ([ReDrafter] "The Full Speculative Decoding Loop", Step 5, rejection
+// sampling; [ResiSpec] section 4, sequential checking).  The acceptance, stop
+// node and next token equal k_vselect's in the same mode; only the tested
+// nodes (children of nodes whose rows are read) get decision, p_tok and q_tok.
+// P workgroups per sequence split every scanned row into aligned slices: each
+// scans its slice of a batch of rows for (max, lowest argmax, sum exp(l - max)),
+// the P partial statistics are exchanged through tagged words, and every
+// workgroup merges them in workgroup order into the same row statistics.
+// Exchange tags carry a per-call epoch, so the workspace needs no initial
+// contents.
+
+constexpr int kScanBatch = 4;  // 16-byte loads per thread per batch (two batches in flight)
+
+__device__ inline __amdgpu_buffer_rsrc_t scan_rsrc(const float* p, int n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, n * 4, 0x00020000);
+}
+
+__device__ inline void scan_issue(__amdgpu_buffer_rsrc_t rs, f32x4 (&buf)[kScanBatch], int j0) {
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j)
+    buf[j] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   rs, ((j0 + j) * kSelThreads + (int)threadIdx.x) * 16, 0, 0));
+}
+
+// Fold one batch (chunk positions relative to the slice; >= n masked) into a
+// running (max m, lowest argmax a, sum S of exp(l - m)); exp in fp32, S in fp64.
+__device__ inline void scan_fold(const f32x4 (&buf)[kScanBatch], int j0, int n, int base,
+                                 float& m, int& a, double& S) {
+  float bm = -INFINITY;
+  int ba = 0x7fffffff;
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) {
+    const int pos = ((j0 + j) * kSelThreads + (int)threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float l = pos + e < n ? buf[j][e] : -INFINITY;
+      if (l > bm) {
+        bm = l;
+        ba = base + pos + e;
+      }
+    }
+  }
+  if (bm == -INFINITY) return;
+  if (bm > m) {
+    S = m == -INFINITY ? 0.0 : S * (double)__builtin_amdgcn_exp2f((m - bm) * kLog2e);
+    m = bm;
+    a = ba;
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kScanBatch; ++j) {
+    const int pos = ((j0 + j) * kSelThreads + (int)threadIdx.x) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sum += pos + e < n ? __builtin_amdgcn_exp2f((buf[j][e] - m) * kLog2e) : 0.0f;
+  }
+  S += (double)sum;
+}
+
+// Workgroup statistics of row i from the threads' (m, a, S) into sh.sc_*[i].
+__device__ inline void scan_reduce(float m, int a, double S, int i, SelShared& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float wm = m;
+  int wa = a;
+  wave_argmax(wm, wa);
+  if (lane == 0) {
+    sh.wm[wave] = wm;
+    sh.wa[wave] = wa;
+  }
+  __syncthreads();
+  float M = sh.wm[0];
+  int Aa = sh.wa[0];
+  for (int k = 1; k < kSelWaves; ++k) argmax_merge(M, Aa, sh.wm[k], sh.wa[k]);
+  double part = (m == -INFINITY || M == -INFINITY)
+                    ? 0.0
+                    : S * (double)__builtin_amdgcn_exp2f((m - M) * kLog2e);
+  part = wave_sum_f64(part);
+  if (lane == 0) sh.wsum[wave] = part;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int k = 0; k < kSelWaves; ++k) t += sh.wsum[k];
+    sh.sc_m[i] = M;
+    sh.sc_a[i] = Aa;
+    sh.sc_S[i] = t;
+  }
+}
+
+// Statistics of nr (<= kScanRows) rows over this workgroup's slice [lo, lo + n);
+// row_of(i) gives row i's first entry.  Two batches of loads in flight: the
+// next batch (of this row or the next) is issued before the current one is
+// folded.
+template <bool VEC, typename RowOf>
+__device__ __forceinline__ void scan_rows(int nr, RowOf row_of, int lo, int n, SelShared& sh) {
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    const int n_per = ((n >> 2) + kSelThreads - 1) / kSelThreads;  // 16-byte chunks per thread
+    const int nbat = n_per > 0 ? (n_per + kScanBatch - 1) / kScanBatch : 1;
+    const int items = nr * nbat;
+    f32x4 L0[kScanBatch], L1[kScanBatch];
+    auto issue = [&](int q, f32x4 (&buf)[kScanBatch]) {
+      const int i = q / nbat, jb = q - (q / nbat) * nbat;
+      scan_issue(scan_rsrc(row_of(i) + lo, n), buf, jb * kScanBatch);
+    };
+    float m = -INFINITY;
+    int a = 0x7fffffff;
+    double S = 0.0;
+    auto fold_item = [&](int q, const f32x4 (&buf)[kScanBatch]) {
+      const int i = q / nbat, jb = q - (q / nbat) * nbat;
+      scan_fold(buf, jb * kScanBatch, n, lo, m, a, S);
+      if (jb == nbat - 1) {
+        scan_reduce(m, a, S, i, sh);
+        m = -INFINITY;
+        a = 0x7fffffff;
+        S = 0.0;
+      }
+    };
+    issue(0, L0);
+    for (int q = 0; q < items; q += 2) {
+      if (q + 1 < items) issue(q + 1, L1);
+      __builtin_amdgcn_sched_barrier(0);
+      fold_item(q, L0);
+      if (q + 2 < items) issue(q + 2, L0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (q + 1 < items) fold_item(q + 1, L1);
+    }
+  } else {
+    for (int i = 0; i < nr; ++i) {
+      const float* row = row_of(i);
+      float m = -INFINITY;
+      int a = 0x7fffffff;
+      double S = 0.0;
+      for (int v = tid; v < n; v += kSelThreads) {
+        const float l = row[lo + v];
+        if (l > m) {
+          S = m == -INFINITY ? 0.0 : S * (double)__builtin_amdgcn_exp2f((m - l) * kLog2e);
+          m = l;
+          a = lo + v;
+        }
+        if (l != -INFINITY) S += (double)__builtin_amdgcn_exp2f((l - m) * kLog2e);
+      }
+      scan_reduce(m, a, S, i, sh);
+    }
+  }
+}
+
+template <int MODE, bool VEC>
+__global__ __launch_bounds__(kSelThreads) void k_vrwalk(SelArgs A) {
+  __shared__ SelShared sh;
+  __shared__ int s_bad;
+  const int b = blockIdx.x / A.P;
+  const int w = blockIdx.x - b * A.P;
+  const int tid = threadIdx.x;
+  const int T_cap = A.T_cap, V = A.V, P = A.P;
+  const int pb = walk_p_bound(V);
+  unsigned char* area = A.sync + (size_t)b * walk_stride(V);
+  SeqSync sy;
+  sy.slot = reinterpret_cast<uint64_t*>(area);
+  sy.wslot = reinterpret_cast<uint64_t*>(area + (size_t)pb * 2 * 4 * 8);
+  sy.pmax = pb;
+  sy.P = P;
+  sy.w = w;
+  sy.rounds = 0;
+  sy.tag_base = A.tag_base;
+  sy.status = A.status;
+  const bool lead = w == 0;
+  const size_t nb = (size_t)b * T_cap;
+  const int lo = w * A.slice;
+  const int n = max(0, min(A.slice, V - lo));
+  static_assert(kSelThreads >= SPEC_MAX_TREE, "one tree row per thread");
+
+  // ---------------------------------------------------------------- tree
+  const int T_in = A.n_nodes[b];
+  int my_par = -1, my_tok = 0, my_dep = 0, my_row = 0;
+  if (tid < T_cap) {
+    my_par = tid == 0 ? -1 : A.parent[nb + tid];
+    my_tok = A.token[nb + tid];
+    my_dep = tid == 0 ? 0 : A.depth[nb + tid];
+    my_row = A.dft_row[nb + tid];
+  }
+  int T = T_in < 1 ? 1 : (T_in > T_cap ? T_cap : T_in);
+  for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) {
+    sh.nch[t] = 0;
+    sh.dec[t] = -1;
+    sh.pt[t] = 0.0;
+    sh.qt[t] = 0.0;
+  }
+  if (tid == 0) {
+    sh.near_count = 0;
+    s_bad = (T_in < 1 || T_in > T_cap) ? SPEC_DEV_BAD_TREE : 0;
+  }
+  __syncthreads();
+  if (tid < T) {
+    sh.par[tid] = my_par;
+    sh.tok[tid] = my_tok;
+    sh.dep[tid] = my_dep;
+    sh.row[tid] = my_row;
+  }
+  __syncthreads();
+  // the validation of k_vselect: a bad sequence accepts nothing and takes the
+  // greedy token at the root
+  for (int t = tid + 1; t < T; t += kSelThreads) {
+    const int p = sh.par[t];
+    if (p < 0 || p >= t) {
+      atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+    } else {
+      if (sh.dep[t] != sh.dep[p] + 1) atomicOr(&s_bad, SPEC_DEV_BAD_TREE);
+      atomicAdd(&sh.nch[p], 1);
+    }
+    if (sh.tok[t] < 0 || sh.tok[t] >= V) atomicOr(&s_bad, SPEC_DEV_BAD_TOKEN);
+  }
+  __syncthreads();
+  for (int t = tid; t < T; t += kSelThreads) {
+    if (sh.nch[t] == 0) continue;
+    const int r = sh.row[t];
+    if (r < 0 || r >= A.Rr) atomicOr(&s_bad, SPEC_DEV_BAD_ROW);
+  }
+  __syncthreads();
+  const bool bad = s_bad != 0;
+  if (bad) {
+    if (lead && tid == 0) raise_status(A.status, s_bad);
+    T = 1;
+    for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) sh.nch[t] = 0;
+    __syncthreads();
+  }
+
+  // ---------------------------------------------------------------- row scans
+  // Nodes sh.scan_node[i0 .. i0 + nn): target rows, and with_q their draft
+  // rows; the merged statistics land in m_p / arg_p / S_p (and m_q / S_q).
+  auto scan_nodes = [&](int i0, int nn, bool with_q) {
+    const int nr = with_q ? 2 * nn : nn;
+    auto row_of = [&](int i) -> const float* {
+      const int node = sh.scan_node[i0 + (with_q ? (i >> 1) : i)];
+      if (with_q && (i & 1)) return A.dft + ((size_t)b * A.Rr + sh.row[node]) * V;
+      return A.tgt + (nb + node) * V;
+    };
+    scan_rows<VEC>(nr, row_of, lo, n, sh);
+    __syncthreads();
+    if (tid < nr) {
+      const uint64_t sb = (uint64_t)__double_as_longlong(sh.sc_S[tid]);
+      sh.xw_mine[4 * tid] = __float_as_uint(sh.sc_m[tid]);
+      sh.xw_mine[4 * tid + 1] = (uint32_t)sh.sc_a[tid];
+      sh.xw_mine[4 * tid + 2] = (uint32_t)sb;
+      sh.xw_mine[4 * tid + 3] = (uint32_t)(sb >> 32);
+    }
+    const int nw = 4 * nr;
+    sy.exchange_words(sh.xw_mine, nw, sh.xw_all);
+    if (tid < nr) {
+      // merge the P slices in workgroup order (ascending vocabulary)
+      float M = -INFINITY;
+      int Aa = 0x7fffffff;
+      for (int k = 0; k < P; ++k)
+        argmax_merge(M, Aa, __uint_as_float(sh.xw_all[k * nw + 4 * tid]),
+                     (int)sh.xw_all[k * nw + 4 * tid + 1]);
+      double S = 0.0;
+      for (int k = 0; k < P; ++k) {
+        const float mk = __uint_as_float(sh.xw_all[k * nw + 4 * tid]);
+        const uint64_t sb = ((uint64_t)sh.xw_all[k * nw + 4 * tid + 3] << 32) |
+                            sh.xw_all[k * nw + 4 * tid + 2];
+        if (mk != -INFINITY) S += __longlong_as_double((long long)sb) * exp((double)mk - (double)M);
+      }
+      const int node = sh.scan_node[i0 + (with_q ? (tid >> 1) : tid)];
+      if (with_q && (tid & 1)) {
+        sh.m_q[node] = M;
+        sh.S_q[node] = S;
+      } else {
+        sh.m_p[node] = M;
+        sh.arg_p[node] = Aa;
+        sh.S_p[node] = S;
+      }
+    }
+    __syncthreads();
+  };
+  // p and q of the own token of every child of the nodes in the batch, from
+  // logits gathered before the scan (fp64 exp, merged sums)
+  auto child_of_batch = [&](int t, int i0, int nn) {
+    if (t < 1 || t >= T) return false;
+    const int p = sh.par[t];
+    for (int i = 0; i < nn; ++i)
+      if (sh.scan_node[i0 + i] == p) return true;
+    return false;
+  };
+
+  RowPair rp{};
+  RowCache rc;
+  cache_range(rc, V, sy);
+  int stop = 0, draw_k = -1;
+  bool cached = false;
+
+  if (MODE == SPEC_REJECT_PATH) {
+    // ------------------------------------------------------------ per-path walk
+    if (tid == 0) {
+      sh.front[0] = 0;
+      sh.n_front = 1;
+    }
+    __syncthreads();
+    int d = 0;
+    while (sh.n_front > 0) {
+      const int nf = sh.n_front;
+      stop = sh.front[0];  // the lowest-index survivor of this depth
+      if (tid == 0) {
+        int c = 0;
+        for (int i = 0; i < nf; ++i)
+          if (sh.nch[sh.front[i]] > 0) sh.scan_node[c++] = sh.front[i];
+        sh.n_scan = c;
+      }
+      __syncthreads();
+      const int ns = sh.n_scan;
+      for (int i0 = 0; i0 < ns; i0 += kScanRows / 2) {
+        const int nn = min(kScanRows / 2, ns - i0);
+        const bool mine = child_of_batch(tid, i0, nn);
+        double lp_own = 0.0, lq_own = 0.0;
+        if (mine) {
+          const int sp = sh.par[tid], x = sh.tok[tid];
+          lp_own = A.tgt[(nb + sp) * V + x];
+          lq_own = A.dft[((size_t)b * A.Rr + sh.row[sp]) * V + x];
+        }
+        scan_nodes(i0, nn, true);
+        if (mine) {
+          const int t = tid, sp = sh.par[t];
+          const double p = exp(lp_own - (double)sh.m_p[sp]) / sh.S_p[sp];
+          const double q = exp(lq_own - (double)sh.m_q[sp]) / sh.S_q[sp];
+          sh.pt[t] = p;
+          sh.qt[t] = q;
+          const double ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
+          const double u = (double)A.u_node[nb + t];
+          sh.dec[t] = u < ratio;
+          if (fabs(ratio - u) < kNearTie) atomicAdd(&sh.near_count, 1);
+        }
+        __syncthreads();
+      }
+      // next frontier: the accepted children of this depth, in node order
+      if (tid < kWave) {
+        const int t0 = tid, t1 = tid + kWave;
+        const bool a0 = t0 >= 1 && t0 < T && sh.dep[t0] == d + 1 && sh.dec[t0] == 1;
+        const bool a1 = t1 < T && sh.dep[t1] == d + 1 && sh.dec[t1] == 1;
+        const uint64_t m0 = __ballot(a0), m1 = __ballot(a1);
+        const uint64_t below = (tid == 0) ? 0ull : (~0ull >> (64 - tid));
+        const int n0 = __popcll(m0);
+        if (a0) sh.front[__popcll(m0 & below)] = t0;
+        if (a1) sh.front[n0 + __popcll(m1 & below)] = t1;
+        if (tid == 0) sh.n_front = n0 + __popcll(m1);
+      }
+      __syncthreads();
+      ++d;
+    }
+    if (!bad && sh.nch[stop] > 0) {
+      // every child of the stop node was rejected: norm(max(0, p_s - q_s)),
+      // from the rows its frontier scan read
+      rp.lp = A.tgt + (nb + stop) * V;
+      rp.mp = sh.m_p[stop];
+      rp.lq = A.dft + ((size_t)b * A.Rr + sh.row[stop]) * V;
+      rp.mq = sh.m_q[stop];
+      if (A.cache) {
+        cache_load(rc, rp, true, true, sy, sh);
+        cached = true;
+      } else {
+        pass_normalisers(rp, true, sy, sh, V);
+      }
+      draw_k = 0;
+    }
+  } else {
+    // ------------------------------------------------------------ sequential walk
+    int s = 0;
+    while (!bad) {
+      if (sh.nch[s] > 0) {
+        if (tid == 0) sh.scan_node[0] = s;
+        __syncthreads();
+        const bool mine = tid >= 1 && tid < T && sh.par[tid] == s;
+        double lp_own = 0.0, lq_own = 0.0;
+        if (mine) {
+          lp_own = A.tgt[(nb + s) * V + sh.tok[tid]];
+          lq_own = A.dft[((size_t)b * A.Rr + sh.row[s]) * V + sh.tok[tid]];
+        }
+        scan_nodes(0, 1, true);
+        if (mine) {
+          sh.pt[tid] = exp(lp_own - (double)sh.m_p[s]) / sh.S_p[s];
+          sh.qt[tid] = exp(lq_own - (double)sh.m_q[s]) / sh.S_q[s];
+        }
+        __syncthreads();
+      }
+      int next_s = s;
+      if (test_children_seq(A, nb, s, T, rp, rc, sy, sh, draw_k, cached, next_s)) {
+        s = next_s;
+        continue;
+      }
+      stop = s;
+      break;
+    }
+  }
+  if (bad || sh.nch[stop] == 0) {
+    // a stop node without children (or a bad sequence's root): its target row
+    if (tid == 0) sh.scan_node[0] = stop;
+    __syncthreads();
+    scan_nodes(0, 1, false);
+    draw_k = -1;
+    cached = false;
+  }
+
+  // ---------------------------------------------------------------- final token
+  int next = 0, cdf_near = 0;
+  const bool have_next = final_token(false, A, nb, stop, bad, draw_k, cached, rp, rc, sy, sh,
+                                     lead, next, cdf_near);
+
+  // ---------------------------------------------------------------- outputs
+  const int near_total = sh.near_count + cdf_near;
+  if (have_next && tid == 0) {
+    A.next_token[b] = next;
+    if (A.near_tie) A.near_tie[b] = near_total;
+  }
+  if (!lead) return;
+  if (tid == 0) A.acc_len[b] = sh.dep[stop];
+  for (int t = tid; t < T_cap; t += kSelThreads) {
+    int pv = -1;
+    if (!bad && t <= sh.dep[stop]) {
+      int cur = stop;
+      while (sh.dep[cur] > t) cur = sh.par[cur];
+      pv = cur;
+    }
+    if (bad && t == 0) pv = 0;
+    A.acc_path[nb + t] = pv;
+    if (A.decision) A.decision[nb + t] = (int8_t)((t < T && !bad) ? sh.dec[t] : -1);
+    // only tested nodes carry p and q (a sequential walk gathers them for
+    // every child of a node it reads, also those after the accepted one)
+    const bool tested = t < T && !bad && sh.dec[t] >= 0;
+    if (A.p_tok) A.p_tok[nb + t] = tested ? (float)sh.pt[t] : 0.0f;
+    if (A.q_tok) A.q_tok[nb + t] = tested ? (float)sh.qt[t] : 0.0f;
   }
 }
 
@@ -1099,6 +1638,64 @@ int choose_p(int mode, int B, int V) {
   return P;
 }
 
+// Largest P with B * P co-resident walk workgroups, at most kMaxP, and at
+// least 2048 vocabulary entries per workgroup.
+int choose_walk_p(int B, int V) {
+  thread_local int cached_capacity = -1;  // per host thread: no shared state
+  thread_local int cached_device = -1;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (cached_device != dev) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu, reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, true>),
+            kSelThreads, 0) != hipSuccess)
+      return 1;
+    cached_capacity = cus * per_cu;
+    cached_device = dev;
+  }
+  int P = cached_capacity / (B > 0 ? B : 1);
+  if (P > walk_p_bound(V)) P = walk_p_bound(V);
+  if (P < 1) P = 1;
+  return P;
+}
+
+int launch_reject_walk(int mode, SelArgs A, hipStream_t s) {
+  // 16-byte chunk offsets of a row slice must fit the 32-bit buffer range
+  if ((long long)A.V * 4 > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
+  A.P = choose_walk_p(A.B, A.V);
+  int slice = (A.V + A.P - 1) / A.P;
+  A.slice = (slice + 3) & ~3;  // slices start on 16-byte boundaries of 16-byte-aligned rows
+  {
+    const int cslice = (A.V + A.P - 1) / A.P;  // the draw's slicing (slice_of)
+    A.cache = (cslice + kSelThreads - 1) / kSelThreads <= kCacheE ? 1 : 0;
+  }
+  // a new tag base for every call (bits 12..31, never 0): exchange words left
+  // by an earlier call never match this call's tags
+  static std::atomic<uint32_t> calls{0};
+  uint32_t e = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0xfffffu;
+  if (e == 0) e = 1;
+  A.tag_base = e << 12;
+  const bool vec = (A.V % 4 == 0) && aligned(A.tgt, 16) && aligned(A.dft, 16);
+  const void* fn;
+  if (mode == SPEC_REJECT_PATH_WALK)
+    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, true>)
+             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, false>);
+  else
+    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, true>)
+             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, false>);
+  void* args[] = {&A};
+  const dim3 grid((unsigned)(A.B * A.P));
+  hipError_t err;
+  if (A.P > 1)
+    err = launch_meeting_kernel(fn, grid, dim3(kSelThreads), args, s);
+  else
+    err = hipLaunchKernel(fn, grid, dim3(kSelThreads), args, 0, s);
+  return err == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 template <int EPT>
 void launch_stats(const VerifyPlan& pl, bool vec, int B, int T_cap, int V, int Rr,
                   const float* tgt, const float* dft, const int32_t* n_nodes,
@@ -1120,6 +1717,9 @@ using namespace spec;
 
 extern "C" size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R) {
   if (mode == SPEC_GREEDY_WALK && B >= 1) return verify_walk_workspace_size(B);
+  if ((mode == SPEC_REJECT_PATH_WALK || mode == SPEC_REJECT_RECURSIVE_WALK) && B >= 1 &&
+      T_cap >= 1 && V >= 1)
+    return (size_t)B * walk_stride(V);
   if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE || B < 1 || T_cap < 1 || V < 1)
     return 0;
   const VerifyPlan pl = make_plan(mode, B, T_cap, V, R);
@@ -1133,13 +1733,41 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
                            int32_t* acc_path, int32_t* next_token, float* p_tok, float* q_tok,
                            int8_t* decision, int32_t* near_tie, void* ws, size_t ws_bytes,
                            int32_t* status, void* stream) {
-  if (mode < SPEC_GREEDY || mode > SPEC_GREEDY_WALK) return SPEC_ERR_INVALID;
+  if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE_WALK) return SPEC_ERR_INVALID;
   if (B < 0 || T_cap < 1 || V < 1 || R < 0) return SPEC_ERR_INVALID;
   if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
   if (B == 0) return SPEC_OK;
   if (!tgt || !n_nodes || !parent || !token || !depth || !acc_len || !acc_path || !next_token)
     return SPEC_ERR_INVALID;
   status = status_or_library(status);
+  if (mode == SPEC_REJECT_PATH_WALK || mode == SPEC_REJECT_RECURSIVE_WALK) {
+    if (!dft || !dft_row || R < 1 || !u_node || !u_final) return SPEC_ERR_INVALID;
+    if (!ws || ws_bytes < (size_t)B * walk_stride(V) || !aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
+    SelArgs A{};
+    A.B = B;
+    A.T_cap = T_cap;
+    A.V = V;
+    A.Rr = R;
+    A.tgt = tgt;
+    A.dft = dft;
+    A.dft_row = dft_row;
+    A.n_nodes = n_nodes;
+    A.parent = parent;
+    A.token = token;
+    A.depth = depth;
+    A.u_node = u_node;
+    A.u_final = u_final;
+    A.sync = static_cast<unsigned char*>(ws);
+    A.acc_len = acc_len;
+    A.acc_path = acc_path;
+    A.next_token = next_token;
+    A.p_tok = p_tok;
+    A.q_tok = q_tok;
+    A.decision = decision;
+    A.near_tie = near_tie;
+    A.status = status;
+    return launch_reject_walk(mode, A, as_stream(stream));
+  }
   if (mode == SPEC_GREEDY_WALK)
     return launch_verify_walk(B, T_cap, V, tgt, n_nodes, parent, token, depth, acc_len,
                               acc_path, next_token, p_tok, q_tok, decision, near_tie, ws,
@@ -1256,7 +1884,7 @@ extern "C" int spec_verify_noalloc(int mode, int B, int T_cap, int V, int R, con
                                    int32_t* acc_path, int32_t* next_token, float* p_tok,
                                    float* q_tok, int8_t* decision, int32_t* near_tie,
                                    int32_t* status, void* stream) {
-  if (mode < SPEC_GREEDY || mode > SPEC_GREEDY_WALK) return SPEC_ERR_INVALID;
+  if (mode < SPEC_GREEDY || mode > SPEC_REJECT_RECURSIVE_WALK) return SPEC_ERR_INVALID;
   if (B < 0 || T_cap < 1 || V < 1 || R < 0) return SPEC_ERR_INVALID;
   if (T_cap > SPEC_MAX_TREE) return SPEC_ERR_CAPACITY;
   if (B == 0) return SPEC_OK;
