@@ -45,7 +45,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive | greedy_walk")
+    ap.add_argument("--mode", default=None, help="greedy | reject_path | reject_recursive | "
+                    "greedy_walk | reject_path_walk | reject_recursive_walk")
     ap.add_argument("--sets", type=int, default=0, help="input sets to rotate over (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-s", type=float, default=20.0)
@@ -110,31 +111,58 @@ def attention_flops(inp, n_nodes):
     return total
 
 
-# Greedy acceptance has two verify modes with the same accepted path and next
-# token: the one-pass verify (every row read once, every node tested) and the
-# walk (only the rows of surviving nodes).  The walk pays per tree depth in
-# meeting latency and wins where the rows are many and large: 64 sequences of
-# a 128000-entry vocabulary (about half the verify time).  On the
-# single-sequence 32k workload the two are within a few percent, and the
-# one-pass verify, which tests every node, is kept.
-FASTEST_MODE = {2: "greedy_walk"}
+# Each acceptance rule has a one-pass verify (every needed row read once, every
+# node tested) and a walk (only the rows of nodes whose path is accepted, a
+# dependent round per tree depth).  The greedy walk is the faster one on both
+# greedy workloads (64 sequences of 128000 logits: 46 against 103 us; one
+# sequence of 32000: 8.4 against 10.9 us).  The rejection walks read fewer bytes
+# (70B-class GQA: 319 against 570 MB; 32k multi-candidate: 11 against 134 MB)
+# but are bound by their per-sequence rounds (249 against 127 us and 109
+# against 84 us), so the one-pass rejection modes stay the default there.
+FASTEST_MODE = {1: "greedy_walk", 2: "greedy_walk"}
+# each verify mode's other formulation (the same acceptance), timed beside it
+ALTERNATIVE = {"greedy": "greedy_walk", "greedy_walk": "greedy",
+               "reject_path": "reject_path_walk", "reject_path_walk": "reject_path",
+               "reject_recursive": "reject_recursive_walk",
+               "reject_recursive_walk": "reject_recursive"}
 
 
-def verify_bytes(inp, n_nodes, parent, dft_row, mode, decision=None):
+def verify_bytes(inp, n_nodes, parent, dft_row, mode, decision=None, acc_len=None,
+                 acc_path=None):
     """Algorithmic HBM bytes of one spec_verify launch.
 
-    One pass over every needed row: every target row of the tree (any node can
-    be the stop node) and, in the rejection modes, every draft row of a node
-    with children.  The greedy walk reads one target row per node whose path is
-    accepted: the root and every accepted tested node (decision == 1).
+    One-pass modes: every needed row once, i.e. every target row of the tree
+    (any node can be the stop node) and, in the rejection modes, every draft
+    row of a node with children.  The walks read only what the decisions need:
+    the greedy walk one target row per node whose path is accepted (the root
+    and every accepted tested node); the rejection walks a target and a draft
+    row per visited node with children (per-path: every node whose path is
+    accepted; sequential: the nodes of the accepted path), plus the stop
+    node's target row when it has no children.
     """
     V = inp["V"]
     total = 0
     for b in range(inp["B"]):
+        T = int(n_nodes[b])
         if mode == "greedy_walk":
             total += (1 + int((decision[b] == 1).sum())) * V * 4
             continue
-        T = int(n_nodes[b])
+        if mode in ("reject_path_walk", "reject_recursive_walk"):
+            par = parent[b]
+            n_child = np.bincount(par[1:T], minlength=T)
+            if mode == "reject_path_walk":
+                surv = np.zeros(T, bool)
+                surv[0] = True
+                for t in range(1, T):
+                    surv[t] = decision[b, t] == 1 and surv[par[t]]
+                visited = np.flatnonzero(surv)
+            else:
+                visited = acc_path[b, :int(acc_len[b]) + 1]
+            rows = 2 * int(sum(1 for t in visited if n_child[t] > 0))
+            stop = int(acc_path[b, int(acc_len[b])])
+            rows += 1 if n_child[stop] == 0 else 0
+            total += rows * V * 4
+            continue
         total += T * V * 4
         if mode not in ("greedy", "greedy_walk"):
             has_child = set(int(p) for p in parent[b, 1:T])
@@ -256,13 +284,19 @@ def main():
     brk = {"build": batch_us([st.p_build for st in rot]),
            "attention": batch_us([st.p_attention for st in rot]),
            "verify": batch_us([st.p_verify for st in rot])}
-    one_pass = None
-    if mode == "greedy_walk":
-        # the one-pass greedy verify on the same trees and rows: every target row
-        # read once and every node tested (the walk reads only surviving nodes' rows)
-        calls = [st.prepare_verify_mode("greedy", stream) for _, st in steps_all]
-        one_pass = batch_us([calls[i % n_sets] for i in range(n_roof)])
-        brk["verify_one_pass_greedy"] = one_pass
+    # the same acceptance by the other verify formulation on the same trees and
+    # rows: the one-pass mode (every needed row read once, every node tested)
+    # beside a walk (only the rows of nodes whose path is accepted), and back
+    alt_mode = ALTERNATIVE[mode]
+    calls = [st.prepare_verify_mode(alt_mode, stream) for _, st in steps_all]
+    alt_us = batch_us([calls[i % n_sets] for i in range(n_roof)])
+    torch.cuda.synchronize()
+    alt_bytes = float(np.mean([
+        verify_bytes(inp, st.n_nodes.cpu().numpy(), st.parent.cpu().numpy(),
+                     inp["dft_row"], alt_mode, st.decision.cpu().numpy(),
+                     st.acc_len.cpu().numpy(), st.acc_path.cpu().numpy())
+        for inp, st in steps_all]))
+    brk["verify_" + alt_mode] = alt_us
     # (each commit on a fresh copy of the context lengths, used once: the call
     # is warm from the steps already)
     uses_c = -(-n_roof // n_sets)
@@ -292,9 +326,8 @@ def main():
         a_flops.append(attention_flops(inp, nn))
         v_bytes.append(verify_bytes(inp, nn, st.parent.cpu().numpy(),
                                     inp["dft_row"] if inp["dft_row"] is not None else None, mode,
-                                    st.decision.cpu().numpy()))
-    v1_bytes = [verify_bytes(inp, st.n_nodes.cpu().numpy(), None, None, "greedy")
-                for inp, st in steps_all]
+                                    st.decision.cpu().numpy(), st.acc_len.cpu().numpy(),
+                                    st.acc_path.cpu().numpy()))
     n_accept = [int(st.acc_len.sum().item()) + st.B for _, st in steps_all]
     a_avg = float(np.mean([a_bytes[i % n_sets] for i in range(n_roof)]))
     v_avg = float(np.mean([v_bytes[i % n_sets] for i in range(n_roof)]))
@@ -348,12 +381,12 @@ def main():
                 / HBM_PEAK_GBPS,
         },
         "device_status": status,
-        **({"verify_one_pass_greedy": {
-            "avg_call_us": one_pass, "bytes_per_launch": float(np.mean(v1_bytes)),
-            "GBps": float(np.mean(v1_bytes)) / (one_pass * 1e-6) / 1e9,
-            "note": "one-pass greedy verify on the same trees: every target row read, every "
-                    "node tested; the step uses the greedy walk, same accepted path"}}
-           if one_pass is not None else {}),
+        "verify_alternative": {
+            "mode": alt_mode, "avg_call_us": alt_us, "bytes_per_launch": alt_bytes,
+            "GBps": alt_bytes / (alt_us * 1e-6) / 1e9,
+            "note": "the other verify formulation of the same acceptance on the same trees "
+                    "(one-pass: every needed row read, every node tested; walk: only the rows "
+                    "of nodes whose path is accepted); same accepted path and next token"},
         # beside `value`: verified nodes per second of attention + verify time
         # only, and accepted tokens (acc_len + 1 per sequence) per step time
         "verified_tokens_per_s_attention_verify":

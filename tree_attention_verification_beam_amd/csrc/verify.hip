@@ -357,23 +357,40 @@ struct SeqSync {
       uint64_t* base = wslot + (size_t)(rounds & 1) * pmax * kXWords;
       for (int i = lane; i < nw; i += 64)
         store_coherent(base + (size_t)w * kXWords + i, ((uint64_t)tag << 32) | mine[i]);
-      // every workgroup's words, lane-strided
-      const int n = P * kXWords;
+      // every workgroup's words, lane-strided: all loads of a polling round
+      // are issued together (one coherent round trip per round)
+      constexpr int kPer = kMaxP * kXWords / 64;
+      const int n = P * nw;
+      uint64_t v[kPer];
+      bool ok[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        ok[j] = lane + 64 * j >= n;
+        v[j] = 0;
+      }
       int spins = 0;
-      for (int i0 = 0; i0 < n; i0 += 64) {
-        const int i = i0 + lane;
-        const int wi = i / kXWords, k = i - wi * kXWords;
-        bool ok = i >= n || k >= nw;
-        uint64_t v = 0;
-        while (!ok) {
-          v = load_coherent(base + i);
-          ok = (uint32_t)(v >> 32) == tag;
-          if (!ok && ++spins > (1 << 22)) {
-            raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
-            break;
-          }
+      for (;;) {
+        bool done = true;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int i = lane + 64 * j;
+          if (!ok[j]) v[j] = load_coherent(base + (size_t)(i / nw) * kXWords + (i - (i / nw) * nw));
         }
-        if (i < n && k < nw) all[wi * nw + k] = (uint32_t)v;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          if (!ok[j]) ok[j] = (uint32_t)(v[j] >> 32) == tag;
+          done = done && ok[j];
+        }
+        if (done) break;
+        if (++spins > (1 << 22)) {
+          raise_status(status, SPEC_DEV_SYNC_TIMEOUT);
+          break;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = lane + 64 * j;
+        if (i < n) all[i] = (uint32_t)v[j];
       }
     }
     __syncthreads();
