@@ -31,6 +31,7 @@
 //
 // fp32 path: one wavefront per output row, plain FMA, for the small fp32 case.
 #include "common.hpp"
+#include "tile_mask.hpp"
 
 namespace spec {
 namespace {
@@ -402,22 +403,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // bit p <-> key kt0 + p: context keys before ctx, tree keys whose ancestor bit
   // is set, and nothing at or past k_end.  All shift amounts are uniform.
   auto tile_vis = [&](int i, int kt0) -> uint64_t {
-    const int nctx = ctx - kt0;  // tile keys before the tree
-    uint64_t bits;
-    if (nctx >= kKeyTile) {
-      bits = ~0ull;
-    } else if (nctx >= 0) {
-      bits = (nctx > 0 ? (~0ull >> (64 - nctx)) : 0ull) | (mask0[i] << nctx);
-    } else {
-      const int sh = -nctx;  // tree index of the tile's first key
-      bits = sh >= 128 ? 0ull
-             : sh >= 64 ? (mask1[i] >> (sh - 64))
-             : sh == 0  ? mask0[i]
-                        : (mask0[i] >> sh) | (mask1[i] << (64 - sh));
-    }
-    const int nin = k_end - kt0;  // tile keys inside the range
-    if (nin < kKeyTile) bits &= nin > 0 ? (~0ull >> (64 - nin)) : 0ull;
-    return bits;
+    return tile_vis_bits(ctx - kt0, k_end - kt0, mask0[i], mask1[i]);
   };
 
   auto compute_tile = [&](int stage, int kt0) {
@@ -429,13 +415,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     // (h = (lg >> 1) & 1); bit 32 j + 4 st + e of lvis[i] is that key's
     uint64_t lvis[QT];
     if (need_mask) {
-      const bool h = (lg >> 1) & 1;
 #pragma unroll
-      for (int i = 0; i < QT; ++i) {
-        const uint64_t v = tile_vis(i, kt0) >> (wkey0 + 8 * lg);
-        const uint64_t sw = ((v >> 4) & 0x0F0F0F0F0F0F0F0Full) | ((v << 4) & 0xF0F0F0F0F0F0F0F0ull);
-        lvis[i] = h ? sw : v;
-      }
+      for (int i = 0; i < QT; ++i) lvis[i] = lane_vis_bits(tile_vis(i, kt0), wkey0, lg);
     }
     // Scores of all this wave's keys of the tile first, then one online-softmax
     // step over them (one maximum check and rescale per tile), then P V: the
