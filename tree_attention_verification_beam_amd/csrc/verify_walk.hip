@@ -49,7 +49,7 @@ namespace {
 constexpr int kWalkThreads = 256;
 constexpr int kWalkWaves = kWalkThreads / kWave;
 constexpr int kWalkMaxP = 32;
-constexpr int kBatch = 8;  // 16-byte loads per thread per batch (two batches in flight)
+constexpr int kBatch = 4;  // 16-byte loads per thread per batch (two batches in flight)
 constexpr float kLog2eW = 1.4426950408889634f;
 constexpr int kBufWord3 = 0x00020000;  // buffer resource word 3, raw 32-bit loads
 // per sequence: [2 parities][P][4] tagged entry words
@@ -87,6 +87,7 @@ struct WalkShared {
   float M;
   int arg;
   double S;
+  uint32_t xw[2 * kWave];  // a meeting's entry words
 };
 
 // Fold 4 logits (slice positions pos .. pos+3, those >= n masked) into a running
@@ -259,25 +260,18 @@ __device__ void meet(uint64_t* seq, int P, int w, uint32_t epoch, int round, Wal
         break;
       }
     }
-    // lane 4i + k holds word k of workgroup i (lanes 0..63: workgroups 0..15,
-    // lanes 64.. of the second word: workgroups 16..31); gather workgroup
-    // `lane`'s words with cross-lane reads
-    const uint32_t lo0 = (uint32_t)v0, lo1 = (uint32_t)v1;
-    const int src = 4 * (lane & 15);
-    uint32_t wd[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t x0 = (uint32_t)__shfl((int)lo0, src + k);
-      const uint32_t x1 = (uint32_t)__shfl((int)lo1, src + k);
-      wd[k] = lane < 16 ? x0 : x1;
-    }
+    // word 4i + k (workgroup i, word k) through LDS to lane i
+    sh.xw[lane] = (uint32_t)v0;
+    sh.xw[lane + 64] = (uint32_t)v1;
+    __builtin_amdgcn_wave_barrier();
     float m = -INFINITY;
     int a = 0x7fffffff;
     double S = 0.0;
     if (lane < P) {
-      m = __uint_as_float(wd[0]);
-      a = (int)wd[1];
-      S = __longlong_as_double((long long)(((uint64_t)wd[3] << 32) | wd[2]));
+      m = __uint_as_float(sh.xw[4 * lane]);
+      a = (int)sh.xw[4 * lane + 1];
+      S = __longlong_as_double(
+          (long long)(((uint64_t)sh.xw[4 * lane + 3] << 32) | sh.xw[4 * lane + 2]));
     }
     float M = m;
     int A = a;
