@@ -289,7 +289,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   uint64_t mask0[QT], mask1[QT];
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
-    qt_idx[i] = mt * RG * QT + i * RG + rg;
+    qt_idx[i] = mt * RG * QT + rg * QT + i;
     const int r = min(qt_idx[i] * 16 + l16, M_cap - 1);
     const int t = r / G;
     const int gq = r - t * G;
@@ -309,7 +309,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   if (k_end > n_keys) k_end = n_keys;
   if (bad && sp == 0 && mt == 0 && tid == 0) raise_status(a.status, SPEC_DEV_CTX_RANGE);
 
-  // this wave's query tiles: interleaved over the row groups of the workgroup
+  // this wave's query tiles: consecutive tiles of the row block per row group,
+  // so the dead tiles past a short sequence's rows fall on whole waves, which
+  // skip their tile work and leave their SIMD to the other waves
   bool qt_on[QT];
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
