@@ -345,6 +345,14 @@ int spec_last_device_status(const int32_t *status_dev, void *stream);
  */
 int spec_copy_probe(const void *src, void *dst, size_t n_bytes, void *stream);
 
+/*
+ * spec_read_probe -- plain streaming read of n_bytes (multiple of 16) from src
+ * by n_blocks workgroups of 256 threads, for the platform's achievable read
+ * bandwidth (the ceiling of read-dominated calls such as the attention);
+ * out[n_blocks] (fp32, device) receives one partial sum per workgroup.
+ */
+int spec_read_probe(const void *src, size_t n_bytes, float *out, int n_blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

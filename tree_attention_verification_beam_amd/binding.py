@@ -47,6 +47,7 @@ SIGNATURES = {
     "spec_select_tree": (_c_int, [_c_int] * 3 + [_vp] * 9),
     "spec_last_device_status": (_c_int, [_vp, _vp]),
     "spec_copy_probe": (_c_int, [_vp, _vp, _c_size, _vp]),
+    "spec_read_probe": (_c_int, [_vp, _c_size, _vp, _c_int, _vp]),
 }
 
 _lib = None
@@ -184,6 +185,11 @@ def spec_select_tree(B, N, N_keep, cand_parent, cand_token, cand_logp, keep_pare
 def spec_copy_probe(src, dst, n_bytes, stream=None):
     rc = load().spec_copy_probe(_ptr(src), _ptr(dst), n_bytes, _stream(stream))
     _check("spec_copy_probe", rc)
+
+
+def spec_read_probe(src, n_bytes, out, n_blocks, stream=None):
+    rc = load().spec_read_probe(_ptr(src), n_bytes, _ptr(out), n_blocks, _stream(stream))
+    _check("spec_read_probe", rc)
 
 
 def spec_last_device_status(status=None, stream=None) -> int:

@@ -120,6 +120,30 @@ __global__ __launch_bounds__(256) void k_copy_probe(const uint4* __restrict__ sr
     dst[i] = src[i];
 }
 
+// Plain streaming read: every thread sums eight 16-byte loads per step
+// (grid-stride, loads issued before they are added); one word per block keeps
+// the loads alive.
+__global__ __launch_bounds__(256) void k_read_probe(const f32x4* __restrict__ src, size_t n16,
+                                                    float* __restrict__ out) {
+  constexpr int kU = 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + (kU - 1) * stride < n16; i += kU * stride) {
+    f32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc += v[u];
+  }
+  for (; i < n16; i += stride) acc += src[i];
+  __shared__ float s_sum[4];
+  const float t = wave_sum_f32(acc[0] + acc[1] + acc[2] + acc[3]);
+  if ((threadIdx.x & 63) == 0) s_sum[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+}
+
 }  // namespace
 }  // namespace spec
 
@@ -172,6 +196,15 @@ extern "C" int spec_copy_probe(const void* src, void* dst, size_t n_bytes, void*
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(k_copy_probe, dim3((unsigned)blocks), dim3(256), 0, as_stream(stream),
                      static_cast<const uint4*>(src), static_cast<uint4*>(dst), n16);
+  return launch_status();
+}
+
+extern "C" int spec_read_probe(const void* src, size_t n_bytes, float* out, int n_blocks,
+                               void* stream) {
+  if (!src || !out || n_bytes % 16 || !aligned(src, 16) || n_blocks < 1) return SPEC_ERR_INVALID;
+  if (n_bytes == 0) return SPEC_OK;
+  hipLaunchKernelGGL(k_read_probe, dim3((unsigned)n_blocks), dim3(256), 0, as_stream(stream),
+                     static_cast<const f32x4*>(src), n_bytes / 16, out);
   return launch_status();
 }
 
