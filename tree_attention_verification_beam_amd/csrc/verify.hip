@@ -1208,7 +1208,8 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
 // Exchange tags carry a per-call epoch, so the workspace needs no initial
 // contents.
 
-constexpr int kScanBatch = 4;  // 16-byte loads per thread per batch (two batches in flight)
+constexpr int kScanBatch = 4;  // 16-byte loads per thread per batch
+constexpr int kScanBufs = 4;   // batches in flight
 
 __device__ inline __amdgpu_buffer_rsrc_t scan_rsrc(const float* p, int n) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, n * 4, 0x00020000);
@@ -1287,9 +1288,8 @@ __device__ inline void scan_reduce(float m, int a, double S, int i, SelShared& s
 }
 
 // Statistics of nr (<= kScanRows) rows over this workgroup's slice [lo, lo + n);
-// row_of(i) gives row i's first entry.  Two batches of loads in flight: the
-// next batch (of this row or the next) is issued before the current one is
-// folded.
+// row_of(i) gives row i's first entry.  kScanBufs batches of loads in flight:
+// the batches of the next rows are issued before the current one is folded.
 template <bool VEC, typename RowOf>
 __device__ __forceinline__ void scan_rows(int nr, RowOf row_of, int lo, int n, SelShared& sh) {
   const int tid = threadIdx.x;
@@ -1297,7 +1297,6 @@ __device__ __forceinline__ void scan_rows(int nr, RowOf row_of, int lo, int n, S
     const int n_per = ((n >> 2) + kSelThreads - 1) / kSelThreads;  // 16-byte chunks per thread
     const int nbat = n_per > 0 ? (n_per + kScanBatch - 1) / kScanBatch : 1;
     const int items = nr * nbat;
-    f32x4 L0[kScanBatch], L1[kScanBatch];
     auto issue = [&](int q, f32x4 (&buf)[kScanBatch]) {
       const int i = q / nbat, jb = q - (q / nbat) * nbat;
       scan_issue(scan_rsrc(row_of(i) + lo, n), buf, jb * kScanBatch);
@@ -1315,14 +1314,20 @@ __device__ __forceinline__ void scan_rows(int nr, RowOf row_of, int lo, int n, S
         S = 0.0;
       }
     };
-    issue(0, L0);
-    for (int q = 0; q < items; q += 2) {
-      if (q + 1 < items) issue(q + 1, L1);
-      __builtin_amdgcn_sched_barrier(0);
-      fold_item(q, L0);
-      if (q + 2 < items) issue(q + 2, L0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (q + 1 < items) fold_item(q + 1, L1);
+    // kScanBufs batches in flight: batch q + kScanBufs - 1 is issued into the
+    // registers batch q - 1 has just left
+    f32x4 L[kScanBufs][kScanBatch];
+#pragma unroll
+    for (int u = 0; u < kScanBufs - 1; ++u)
+      if (u < items) issue(u, L[u]);
+    for (int q0 = 0; q0 < items; q0 += kScanBufs) {
+#pragma unroll
+      for (int u = 0; u < kScanBufs; ++u) {
+        const int q = q0 + u;
+        if (q + kScanBufs - 1 < items) issue(q + kScanBufs - 1, L[(u + kScanBufs - 1) % kScanBufs]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (q < items) fold_item(q, L[u]);
+      }
     }
   } else {
     for (int i = 0; i < nr; ++i) {
@@ -1657,23 +1662,26 @@ int choose_p(int mode, int B, int V) {
 
 // Largest P with B * P co-resident walk workgroups, at most kMaxP, and at
 // least 2048 vocabulary entries per workgroup.
-int choose_walk_p(int B, int V) {
-  thread_local int cached_capacity = -1;  // per host thread: no shared state
-  thread_local int cached_device = -1;
+// (per walk kernel: the two modes differ in registers and so in occupancy)
+int choose_walk_p(int B, int V, const void* fn) {
+  thread_local const void* cached_fn[2] = {nullptr, nullptr};
+  thread_local int cached_capacity[2] = {-1, -1};  // per host thread: no shared state
+  thread_local int cached_device[2] = {-1, -1};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
-  if (cached_device != dev) {
+  int slot = cached_fn[0] == fn ? 0 : (cached_fn[1] == fn ? 1 : -1);
+  if (slot < 0 || cached_device[slot] != dev) {
+    if (slot < 0) slot = cached_fn[0] == nullptr ? 0 : 1;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, true>),
-            kSelThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, 0) != hipSuccess)
       return 1;
-    cached_capacity = cus * per_cu;
-    cached_device = dev;
+    cached_fn[slot] = fn;
+    cached_capacity[slot] = cus * per_cu;
+    cached_device[slot] = dev;
   }
-  int P = cached_capacity / (B > 0 ? B : 1);
+  int P = cached_capacity[slot] / (B > 0 ? B : 1);
   if (P > walk_p_bound(V)) P = walk_p_bound(V);
   if (P < 1) P = 1;
   return P;
@@ -1682,7 +1690,15 @@ int choose_walk_p(int B, int V) {
 int launch_reject_walk(int mode, SelArgs A, hipStream_t s) {
   // 16-byte chunk offsets of a row slice must fit the 32-bit buffer range
   if ((long long)A.V * 4 > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
-  A.P = choose_walk_p(A.B, A.V);
+  const bool vec = (A.V % 4 == 0) && aligned(A.tgt, 16) && aligned(A.dft, 16);
+  const void* fn;
+  if (mode == SPEC_REJECT_PATH_WALK)
+    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, true>)
+             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, false>);
+  else
+    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, true>)
+             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, false>);
+  A.P = choose_walk_p(A.B, A.V, fn);
   int slice = (A.V + A.P - 1) / A.P;
   A.slice = (slice + 3) & ~3;  // slices start on 16-byte boundaries of 16-byte-aligned rows
   {
@@ -1695,14 +1711,6 @@ int launch_reject_walk(int mode, SelArgs A, hipStream_t s) {
   uint32_t e = (calls.fetch_add(1, std::memory_order_relaxed) + 1) & 0xfffffu;
   if (e == 0) e = 1;
   A.tag_base = e << 12;
-  const bool vec = (A.V % 4 == 0) && aligned(A.tgt, 16) && aligned(A.dft, 16);
-  const void* fn;
-  if (mode == SPEC_REJECT_PATH_WALK)
-    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, true>)
-             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_PATH, false>);
-  else
-    fn = vec ? reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, true>)
-             : reinterpret_cast<const void*>(k_vrwalk<SPEC_REJECT_RECURSIVE, false>);
   void* args[] = {&A};
   const dim3 grid((unsigned)(A.B * A.P));
   hipError_t err;
