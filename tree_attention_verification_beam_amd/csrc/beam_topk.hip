@@ -221,13 +221,13 @@ __global__ __launch_bounds__(kTopThreads) void k_topk_slices(int K_in, int V, in
 #pragma unroll
     for (int u = 0; u < U; ++u)
       x[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, (u * kTopThreads + tid) * 16, 0, 0));
+                                           rs, (u * kTopThreads + tid) * 16, 0, kLoadOnce));
     for (int c0 = 0; c0 < n_chunks; c0 += U * kTopThreads) {
       // the next step's loads go out before this step's elements are offered
 #pragma unroll
       for (int u = 0; u < U; ++u)
         y[u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             rs, (c0 + (U + u) * kTopThreads + tid) * 16, 0, 0));
+                                             rs, (c0 + (U + u) * kTopThreads + tid) * 16, 0, kLoadOnce));
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll

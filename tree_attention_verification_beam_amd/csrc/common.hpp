@@ -38,6 +38,11 @@ __device__ inline uint64_t load_coherent(const uint64_t* p) {
 }
 __device__ inline void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Cache-policy operand of buffer loads for data that is read once (the K/V
+// tiles of a key range only one workgroup reads, logits rows): non-temporal,
+// so such a stream does not displace lines that other loads will reuse.
+constexpr int kLoadOnce = 2;
+
 // ---------------------------------------------------------------- reductions
 // Cross-lane exchanges without the LDS crossbar: within a 16-lane row, DPP
 // quad permutes (partner l ^ 1, l ^ 2) and row mirrors (partner 7 - l within

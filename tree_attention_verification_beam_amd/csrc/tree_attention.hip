@@ -179,7 +179,7 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
-template <int D, int NW, int QT, int KG, int PF>
+template <int D, int NW, int QT, int KG, int PF, bool ONCE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   constexpr int kThreads = NW * 64;
   constexpr int RG = NW / KG;           // row groups
@@ -233,13 +233,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // zeros for keys at or past `limit`.  So the loads never branch or clamp (a
   // full and a partial tile run the same code, and prefetched loads stay in
   // flight), and keys past the range reach LDS as zeros, to be masked to -inf
-  // before the softmax.  PF register sets keep PF tiles in flight.
+  // before the softmax.  PF register sets keep PF tiles in flight.  When this
+  // workgroup is the only reader of its key range (one row block), the loads
+  // are non-temporal.
   constexpr int OCT = D / 8;
   constexpr int K_TOTAL = kKeyTile * OCT;                          // 16-byte K units per tile
   constexpr int K_UNITS = K_TOTAL / kThreads;                      // per thread
   constexpr int VK = kKeyTile * OCT / kThreads;                    // keys per V unit
   static_assert(K_TOTAL % kThreads == 0 && VK >= 1 && VK <= 4, "tile split");
   constexpr int kRowBytes = D * 2;
+  constexpr int kCpol = ONCE ? kLoadOnce : 0;
 
   int koff[K_UNITS], voff[VK];  // byte offsets inside a tile
 #pragma unroll
@@ -260,10 +263,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     const auto rv = tile_rsrc(vbase, kt0, limit);
 #pragma unroll
     for (int u = 0; u < K_UNITS; ++u)
-      kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, 0));
+      kr[u] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, koff[u], 0, kCpol));
 #pragma unroll
     for (int j = 0; j < VK; ++j)
-      vr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, 0));
+      vr[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rv, voff[j], 0, kCpol));
   };
   // zero the keys of a speculatively loaded tile that lie past `last` (cache
   // slots past the sequence may hold any bits, NaN included)
@@ -816,9 +819,9 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
 
 // ------------------------------------------------------------------ launchers
 
-template <int D, int NW, int QT, int KG, int PF>
+template <int D, int NW, int QT, int KG, int PF, bool ONCE>
 int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
-  auto kern = k_attn_bf16<D, NW, QT, KG, PF>;
+  auto kern = k_attn_bf16<D, NW, QT, KG, PF, ONCE>;
   const int lds = Lds<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
@@ -826,23 +829,18 @@ int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   return launch_status();
 }
 
+// The plans make_plan can choose.  A key range read by one row block only
+// (n_mt == 1) is streamed with non-temporal loads; row blocks that share a key
+// range keep the default policy so the others find its tiles in L2.
 template <int D>
 int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
-#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_)                            \
-  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_)       \
-    return launch_main<D, NW_, QT_, KG_, PF_>(p, args, s);
-  SPEC_ATTN_CASE(4, 1, 2, 1)
-  SPEC_ATTN_CASE(4, 2, 2, 1)
-  SPEC_ATTN_CASE(4, 1, 1, 1)
-  SPEC_ATTN_CASE(4, 2, 1, 1)
+  const bool once = p.n_mt == 1;
+#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_)                                \
+  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_)           \
+    return once ? launch_main<D, NW_, QT_, KG_, PF_, true>(p, args, s)    \
+                : launch_main<D, NW_, QT_, KG_, PF_, false>(p, args, s);
   SPEC_ATTN_CASE(8, 1, 2, 1)
-  SPEC_ATTN_CASE(8, 1, 1, 1)
-  SPEC_ATTN_CASE(8, 2, 1, 1)
-  SPEC_ATTN_CASE(4, 1, 2, 2)
-  SPEC_ATTN_CASE(4, 2, 2, 2)
-  SPEC_ATTN_CASE(4, 1, 1, 2)
   SPEC_ATTN_CASE(8, 1, 2, 2)
-  SPEC_ATTN_CASE(8, 1, 1, 2)
   SPEC_ATTN_CASE(8, 2, 1, 2)
   SPEC_ATTN_CASE(4, 2, 1, 2)
 #undef SPEC_ATTN_CASE

@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
     for (int j = 0; j < EPT / 4; ++j) {
       const int e = base + 4 * (tid + kStatThreads * j);
       idx0[j] = e;
-      f32x4 v4 = e < V ? *reinterpret_cast<const f32x4*>(row + e)
+      f32x4 v4 = e < V ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(row + e))
                        : f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       x[4 * j] = v4[0];
       x[4 * j + 1] = v4[1];
@@ -1220,7 +1220,7 @@ __device__ inline void scan_issue(__amdgpu_buffer_rsrc_t rs, f32x4 (&buf)[kScanB
   for (int j = 0; j < kScanBatch; ++j)
     buf[j] = __builtin_bit_cast(
         f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                   rs, ((j0 + j) * kSelThreads + (int)threadIdx.x) * 16, 0, 0));
+                   rs, ((j0 + j) * kSelThreads + (int)threadIdx.x) * 16, 0, kLoadOnce));
 }
 
 // Fold one batch (chunk positions relative to the slice; >= n masked) into a

@@ -117,7 +117,7 @@ __device__ inline void load_batch(__amdgpu_buffer_rsrc_t rs, f32x4 (&buf)[kBatch
   for (int j = 0; j < kBatch; ++j)
     buf[j] = __builtin_bit_cast(
         f32x4,
-        __builtin_amdgcn_raw_buffer_load_b128(rs, ((j0 + j) * kWalkThreads + tid) * 16, 0, 0));
+        __builtin_amdgcn_raw_buffer_load_b128(rs, ((j0 + j) * kWalkThreads + tid) * 16, 0, kLoadOnce));
 }
 
 // First two batches of a slice's loads (16-byte path); callers overlap them
