@@ -347,9 +347,11 @@ int spec_copy_probe(const void *src, void *dst, size_t n_bytes, void *stream);
 
 /*
  * spec_read_probe -- plain streaming read of n_bytes (multiple of 16) from src
- * by n_blocks workgroups of 256 threads, for the platform's achievable read
- * bandwidth (the ceiling of read-dominated calls such as the attention);
- * out[n_blocks] (fp32, device) receives one partial sum per workgroup.
+ * for the platform's achievable read bandwidth (the ceiling of read-dominated
+ * calls such as the attention): workgroup g of n_blocks (256 threads each)
+ * reads the 256 KiB chunks g, g + n_blocks, ... front to back with
+ * non-temporal loads; out[n_blocks] (fp32, device) receives one partial sum
+ * per workgroup.
  */
 int spec_read_probe(const void *src, size_t n_bytes, float *out, int n_blocks, void *stream);
 

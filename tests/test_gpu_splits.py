@@ -3,8 +3,9 @@
 The context of a (sequence, KV head) is split over workgroups so that the grid
 covers the CUs; a merge kernel then combines the (max, sum, O) partials.  The
 shapes below make the plan choose 1, 2, 4, 21 and 32 splits (the last two with
-two and with one key group), each compared with the oracle within 1e-2 of the
-largest output, with ragged contexts where B > 1.
+two and with one key group) and, for 1024 (sequence, head) streams, 4-wave
+groups; each is compared with the oracle within 1e-2 of the largest output,
+with ragged contexts where B > 1.
 """
 import numpy as np
 import pytest
@@ -23,6 +24,8 @@ CASES = {
     "4 splits": (2, 32, 32, [1000, 777]),
     "21 splits": (1, 1, 1, [4000]),
     "32 splits, GQA": (1, 4, 1, [8000]),
+    # 1024 (sequence, head) streams of at most 32 rows: 4-wave groups
+    "1024 streams": (32, 32, 32, [40 + 7 * i for i in range(32)]),
 }
 
 

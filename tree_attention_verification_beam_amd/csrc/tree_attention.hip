@@ -81,6 +81,10 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
   if (nq <= 4) {
     // few rows: waves pair up on each key tile (two key groups)
     p.KG = 2; p.QT = 1; p.PF = 1;
+    // many independent key streams (the grid runs in several rounds, bound by
+    // the stream rate) and at most 32 rows: 4-wave groups with two tiles of
+    // loads in flight stream faster
+    if (nq <= 2 && (long)B * Hkv >= 4L * kNumCU) { p.NW = 4; p.PF = 2; }
   } else if (nq <= 16) {
     // one row block: two query tiles per wave, two tiles of loads in flight
     p.KG = 1; p.QT = 2; p.PF = 2;
@@ -841,6 +845,7 @@ int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
                 : launch_main<D, NW_, QT_, KG_, PF_, false>(p, args, s);
   SPEC_ATTN_CASE(8, 1, 2, 1)
   SPEC_ATTN_CASE(8, 1, 2, 2)
+  SPEC_ATTN_CASE(4, 1, 2, 2)
   SPEC_ATTN_CASE(8, 2, 1, 2)
   SPEC_ATTN_CASE(4, 2, 1, 2)
 #undef SPEC_ATTN_CASE
