@@ -26,6 +26,7 @@
 //             then holds the same totals and takes the same decisions.  The
 //             grid is sized to be resident at once (occupancy query) and every
 //             wait is bounded.
+#include <algorithm>
 #include <atomic>
 #include <mutex>
 
@@ -302,6 +303,9 @@ struct SelShared {
   double S_q[SPEC_MAX_TREE];
   double pt[SPEC_MAX_TREE];
   double qt[SPEC_MAX_TREE];
+  float u[SPEC_MAX_TREE];       // the nodes' acceptance uniforms (rejection modes)
+  float own_lp[SPEC_MAX_TREE];  // a child's token logits in its parent's target and draft rows
+  float own_lq[SPEC_MAX_TREE];
   int dec[SPEC_MAX_TREE];
   double red[2 * kSelWaves];
   double scan[kSelThreads];
@@ -461,7 +465,19 @@ struct RowPair {
   double invSp, invSq;  // accurate (fp64) normalisers once known
 };
 
-// p(v), q(v) and the residual after k rejections, r_k(v), in fp64.
+// p(v), q(v) and the residual after k rejections, r_k(v), in fp64, from the
+// token's logits lp_v, lq_v in the row pair.
+__device__ inline double eval_r_logits(const RowPair& rp, float lp_v, float lq_v, int k,
+                                       const double* invN, double& qv) {
+  double r = exp((double)lp_v - rp.mp) * rp.invSp;
+  qv = exp((double)lq_v - rp.mq) * rp.invSq;
+  for (int j = 0; j < k; ++j) {
+    const double w = r - qv;
+    r = w > 0.0 ? w * invN[j] : 0.0;
+  }
+  return r;
+}
+
 __device__ inline double eval_r(const RowPair& rp, int v, int k, const double* invN, double& qv) {
   double r = exp((double)rp.lp[v] - rp.mp) * rp.invSp;
   qv = exp((double)rp.lq[v] - rp.mq) * rp.invSq;
@@ -492,6 +508,76 @@ __device__ inline Slice slice_of(int V, int P, int w) {
   return s;
 }
 
+// Sums over the P exchanged slots, in slot order.  The slots are read eight
+// at a time with every read of a group issued before its adds (a loop bounded
+// by P would wait out one LDS round trip per slot); a slot past P adds +0.0,
+// which leaves a sum of non-negative values unchanged.
+__device__ __forceinline__ void slot_sums(const double* slots, int P, double& ta, double& tb) {
+  static_assert(kMaxP % 8 == 0, "whole groups of slots");
+  ta = 0.0;
+  tb = 0.0;
+  for (int i0 = 0; i0 < P; i0 += 8) {
+    double a[8], b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[j] = slots[2 * (i0 + j)];
+      b[j] = slots[2 * (i0 + j) + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ta += i0 + j < P ? a[j] : 0.0;
+      tb += i0 + j < P ? b[j] : 0.0;
+    }
+  }
+}
+
+__device__ __forceinline__ double slot_sum(const double* slots, int P) {
+  double t = 0.0;
+  for (int i0 = 0; i0 < P; i0 += 8) {
+    double a[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = slots[2 * (i0 + j)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t += i0 + j < P ? a[j] : 0.0;
+  }
+  return t;
+}
+
+// The slice holding the draw's threshold thr: the first slot js with weight
+// whose running total passes thr, and the total before it (base); past the
+// end (rounding), the last slot with weight (overshoot).  Slots read as in
+// slot_sums.
+__device__ __forceinline__ bool find_slice(const double* slots, int P, double thr, int& js,
+                                           double& base) {
+  base = 0.0;
+  js = -1;
+  int jlast = -1;
+  double base_last = 0.0;
+  for (int i0 = 0; i0 < P; i0 += 8) {
+    double t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = slots[2 * (i0 + j)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + j;
+      const double ti = t[j];
+      if (i >= P) continue;
+      if (ti > 0.0) {
+        jlast = i;
+        base_last = base;
+      }
+      if (js < 0 && ti > 0.0 && base + ti > thr) js = i;
+      if (js < 0) base += ti;
+    }
+  }
+  const bool overshoot = js < 0;
+  if (overshoot) {
+    js = jlast;
+    base = base_last;
+  }
+  return overshoot;
+}
+
 // Accurate softmax normalisers of a row pair: sum exp(l - m) in fp64 over V.
 __device__ __forceinline__ void pass_normalisers(RowPair& rp, bool with_q, SeqSync& sy, SelShared& sh, int V) {
   const Slice sl = slice_of(V, sy.P, sy.w);
@@ -502,11 +588,8 @@ __device__ __forceinline__ void pass_normalisers(RowPair& rp, bool with_q, SeqSy
   }
   block_sum2_f64(a, b, sh.red);
   sy.exchange(a, b, sh.slots);
-  double ta = 0.0, tb = 0.0;
-  for (int i = 0; i < sy.P; ++i) {
-    ta += sh.slots[2 * i];
-    tb += sh.slots[2 * i + 1];
-  }
+  double ta, tb;
+  slot_sums(sh.slots, sy.P, ta, tb);
   rp.invSp = 1.0 / ta;
   if (with_q) rp.invSq = 1.0 / tb;
   __syncthreads();
@@ -525,8 +608,7 @@ __device__ __forceinline__ double pass_residual_mass(const RowPair& rp, int k, c
   }
   a = block_sum_f64(a, sh.red);
   sy.exchange(a, 0.0, sh.slots);
-  double t = 0.0;
-  for (int i = 0; i < sy.P; ++i) t += sh.slots[2 * i];
+  const double t = slot_sum(sh.slots, sy.P);
   __syncthreads();
   return t;
 }
@@ -547,8 +629,7 @@ __device__ __forceinline__ bool pass_draw(const RowPair& rp, int k, const double
   double excl;
   const double slice_total = block_exclusive_scan_f64(mine, sh.scan, excl);
   sy.exchange(slice_total, 0.0, sh.slots);
-  double total = 0.0;
-  for (int i = 0; i < sy.P; ++i) total += sh.slots[2 * i];
+  const double total = slot_sum(sh.slots, sy.P);
   *total_out = total;
   if (!(total > 0.0)) {
     __syncthreads();
@@ -557,23 +638,9 @@ __device__ __forceinline__ bool pass_draw(const RowPair& rp, int k, const double
   const double thr = u * total;
   const double eps = kCdfNearTie * total;
   // the slice holding the threshold (or, past the end, the last slice with weight)
-  double base = 0.0;
-  int js = -1, jlast = -1;
-  double base_last = 0.0;
-  for (int i = 0; i < sy.P; ++i) {
-    const double ti = sh.slots[2 * i];
-    if (ti > 0.0) {
-      jlast = i;
-      base_last = base;
-    }
-    if (js < 0 && ti > 0.0 && base + ti > thr) js = i;
-    if (js < 0) base += ti;
-  }
-  const bool overshoot = js < 0;
-  if (overshoot) {
-    js = jlast;
-    base = base_last;
-  }
+  int js;
+  double base;
+  const bool overshoot = find_slice(sh.slots, sy.P, thr, js, base);
   __syncthreads();
   if (js != sy.w) return false;
   // the thread holding the threshold
@@ -670,11 +737,8 @@ __device__ __forceinline__ void cache_load(RowCache& c, RowPair& rp, bool with_q
   if (!normalise) return;
   block_sum2_f64(a, bq, sh.red);
   sy.exchange(a, bq, sh.slots);
-  double ta = 0.0, tb = 0.0;
-  for (int i = 0; i < sy.P; ++i) {
-    ta += sh.slots[2 * i];
-    tb += sh.slots[2 * i + 1];
-  }
+  double ta, tb;
+  slot_sums(sh.slots, sy.P, ta, tb);
   rp.invSp = 1.0 / ta;
   rp.invSq = 1.0 / tb;
 #pragma unroll
@@ -695,8 +759,7 @@ __device__ __forceinline__ double cache_residual_mass(const RowCache& c, SeqSync
   }
   a = block_sum_f64(a, sh.red);
   sy.exchange(a, 0.0, sh.slots);
-  double t = 0.0;
-  for (int i = 0; i < sy.P; ++i) t += sh.slots[2 * i];
+  const double t = slot_sum(sh.slots, sy.P);
   __syncthreads();
   return t;
 }
@@ -729,8 +792,7 @@ __device__ __forceinline__ bool cache_draw(const RowCache& c, bool resid, double
   const double slice_total = block_exclusive_scan_f64(mine, sh.scan, excl);
   (void)excl;
   sy.exchange(slice_total, 0.0, sh.slots);
-  double total = 0.0;
-  for (int i = 0; i < sy.P; ++i) total += sh.slots[2 * i];
+  const double total = slot_sum(sh.slots, sy.P);
   *total_out = total;
   if (!(total > 0.0)) {
     __syncthreads();
@@ -738,23 +800,9 @@ __device__ __forceinline__ bool cache_draw(const RowCache& c, bool resid, double
   }
   const double thr = u * total;
   const double eps = kCdfNearTie * total;
-  double base = 0.0;
-  int js = -1, jlast = -1;
-  double base_last = 0.0;
-  for (int i = 0; i < sy.P; ++i) {
-    const double ti = sh.slots[2 * i];
-    if (ti > 0.0) {
-      jlast = i;
-      base_last = base;
-    }
-    if (js < 0 && ti > 0.0 && base + ti > thr) js = i;
-    if (js < 0) base += ti;
-  }
-  const bool overshoot = js < 0;
-  if (overshoot) {
-    js = jlast;
-    base = base_last;
-  }
+  int js;
+  double base;
+  const bool overshoot = find_slice(sh.slots, sy.P, thr, js, base);
   __syncthreads();
   if (js != sy.w) return false;
   __shared__ int s_found_tok, s_found_near, s_last;
@@ -831,6 +879,16 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
     rp.lq = A.dft + ((size_t)b * A.Rr + r) * V;
     rp.mq = sh.m_q[s];
   }
+  // Every child's own logits in both rows, gathered once: the tests after a
+  // rejection read them from LDS instead of a global round trip each (the
+  // loads stay in flight until the first rejection's exchanges are done).
+  const bool own = tid > s && tid < T && sh.par[tid] == s;
+  float own_lp = 0.0f, own_lq = 0.0f;
+  if (own && sh.nch[s] > 1) {
+    own_lp = rp.lp[sh.tok[tid]];
+    own_lq = rp.lq[sh.tok[tid]];
+  }
+  bool own_stored = false;
   int remaining = sh.nch[s];
   for (int ch = s + 1; ch < T && remaining > 0; ++ch) {
     if (sh.par[ch] != s) continue;
@@ -846,10 +904,11 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
       ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
     } else {
       double qv;
-      const double r = eval_r(rp, x, k, invN, qv);
+      const double r = eval_r_logits(rp, sh.own_lp[ch], sh.own_lq[ch], k, invN, qv);
       ratio = qv > 0.0 ? r / qv : (r > 0.0 ? INFINITY : 0.0);
     }
-    const double u = (double)A.u_node[nb + ch];
+    (void)x;
+    const double u = (double)sh.u[ch];  // loaded with the tree
     if (tid == 0 && fabs(ratio - u) < kNearTie) sh.near_count++;
     if (u < ratio) {
       if (tid == 0) sh.dec[ch] = 1;
@@ -866,6 +925,14 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
         pass_normalisers(rp, true, sy, sh, V);
       }
       have_norm = true;
+    }
+    if (!own_stored) {
+      // read at k >= 1, after the residual mass exchange's barriers
+      if (own) {
+        sh.own_lp[tid] = own_lp;
+        sh.own_lq[tid] = own_lq;
+      }
+      own_stored = true;
     }
     if (remaining == 0) {
       // last child rejected: the draw uses max(0, r_k - q) unnormalised
@@ -957,11 +1024,15 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
   // every target row the tree can have (rows past n_nodes are never used).
   const int T_in = A.n_nodes[b];
   int my_par = -1, my_tok = 0, my_dep = 0, my_row = 0;
+  float my_u = 0.0f;
   if (tid < T_cap) {
     my_par = tid == 0 ? -1 : A.parent[nb + tid];
     my_tok = A.token[nb + tid];
     my_dep = tid == 0 ? 0 : A.depth[nb + tid];
-    if (MODE != SPEC_GREEDY) my_row = A.dft_row[nb + tid];
+    if (MODE != SPEC_GREEDY) {
+      my_row = A.dft_row[nb + tid];
+      my_u = A.u_node[nb + tid];
+    }
   }
   const bool staged = MODE == SPEC_GREEDY && T_cap * A.n_chunks <= kMergeEntries;
   if (staged)
@@ -986,6 +1057,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
     sh.tok[tid] = my_tok;
     sh.dep[tid] = my_dep;
     sh.row[tid] = my_row;
+    sh.u[tid] = my_u;
   }
   __syncthreads();
   // validate the tree against the vocabulary and the draft rows; a bad
@@ -1115,7 +1187,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vselect(SelArgs A) {
       } else {
         const double p = sh.pt[t], q = sh.qt[t];
         const double ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
-        const double u = (double)A.u_node[nb + t];
+        const double u = (double)sh.u[t];
         acc = u < ratio;
         if (fabs(ratio - u) < kNearTie) atomicAdd(&sh.near_count, 1);
       }
@@ -1377,11 +1449,13 @@ __global__ __launch_bounds__(kSelThreads) void k_vrwalk(SelArgs A) {
   // ---------------------------------------------------------------- tree
   const int T_in = A.n_nodes[b];
   int my_par = -1, my_tok = 0, my_dep = 0, my_row = 0;
+  float my_u = 0.0f;
   if (tid < T_cap) {
     my_par = tid == 0 ? -1 : A.parent[nb + tid];
     my_tok = A.token[nb + tid];
     my_dep = tid == 0 ? 0 : A.depth[nb + tid];
     my_row = A.dft_row[nb + tid];
+    my_u = A.u_node[nb + tid];
   }
   int T = T_in < 1 ? 1 : (T_in > T_cap ? T_cap : T_in);
   for (int t = tid; t < SPEC_MAX_TREE; t += kSelThreads) {
@@ -1400,6 +1474,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vrwalk(SelArgs A) {
     sh.tok[tid] = my_tok;
     sh.dep[tid] = my_dep;
     sh.row[tid] = my_row;
+    sh.u[tid] = my_u;
   }
   __syncthreads();
   // the validation of k_vselect: a bad sequence accepts nothing and takes the
@@ -1528,7 +1603,7 @@ __global__ __launch_bounds__(kSelThreads) void k_vrwalk(SelArgs A) {
           sh.pt[t] = p;
           sh.qt[t] = q;
           const double ratio = q > 0.0 ? p / q : (p > 0.0 ? INFINITY : 0.0);
-          const double u = (double)A.u_node[nb + t];
+          const double u = (double)sh.u[t];
           sh.dec[t] = u < ratio;
           if (fabs(ratio - u) < kNearTie) atomicAdd(&sh.near_count, 1);
         }
@@ -1642,14 +1717,18 @@ int choose_p(int mode, int B, int V) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
   if (cached_device != dev) {
-    int cus = 0, per_cu = 0;
+    int cus = 0, per_cu = 0, per_cu_path = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 1;
+    // the fewer of the two rejection-mode kernels' resident workgroups per CU
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &per_cu, reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_RECURSIVE>),
+            kSelThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &per_cu_path, reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_PATH>),
             kSelThreads, 0) != hipSuccess)
       return 1;
-    cached_capacity = cus * per_cu;
+    cached_capacity = cus * std::min(per_cu, per_cu_path);
     cached_device = dev;
   }
   int P = cached_capacity / (B > 0 ? B : 1);
