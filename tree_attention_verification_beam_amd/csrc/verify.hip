@@ -135,20 +135,31 @@ __device__ __forceinline__ void block_sum2_f64(double& a, double& b, double* s_r
   b = tb;
 }
 
-// exclusive scan over the block's threads (in thread order), fp64; returns the total
+// exclusive scan over the block's threads (in thread order), fp64; returns the
+// total and leaves every thread's inclusive value in s_buf[tid].  Each wave
+// scans its lanes with shuffles (Hillis-Steele over 64 lanes), then adds the
+// totals of the waves before it.
 __device__ __forceinline__ double block_exclusive_scan_f64(double v, double* s_buf, double& excl) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  s_buf[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const double add = tid >= off ? s_buf[tid - off] : 0.0;
-    __syncthreads();
-    s_buf[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  double inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const double add = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += add;
   }
-  excl = s_buf[tid] - v;
-  const double total = s_buf[kSelThreads - 1];
+  __shared__ double s_wave[kSelWaves];
+  __syncthreads();
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  double before = 0.0, total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) {
+    if (w < wave) before += s_wave[w];
+    total += s_wave[w];
+  }
+  inc += before;
+  s_buf[tid] = inc;
+  excl = inc - v;
   __syncthreads();
   return total;
 }
@@ -311,6 +322,7 @@ struct SelShared {
   double scan[kSelThreads];
   double slots[2 * kMaxP];
   double invN[64];
+  double xsum;  // reduce_exchange's total
   // row-statistics merge: jobs are the needed rows, entries their chunk partials
   Partial ent[kMergeEntries];
   int job_unit[2 * SPEC_MAX_TREE];
@@ -456,6 +468,58 @@ struct SeqSync {
     ++rounds;
   }
 };
+
+// Block sum of x, then its sum over the P workgroups (identical in every
+// workgroup): each wave's sum goes through LDS to wave 0, which publishes the
+// workgroup's total, waits for the others and adds them in a fixed lane order;
+// lane 0 leaves the total in *out and its reciprocal in *inv_out.  Two
+// barriers in all.  Slot words, tags and parities as in SeqSync::exchange.
+__device__ __forceinline__ double reduce_exchange(SeqSync& sy, double x, double* s_red, double* out,
+                                                  double* inv_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  x = wave_sum_f64(x);
+  __syncthreads();
+  if (lane == 0) s_red[wave] = x;
+  __syncthreads();
+  if (tid < 64) {
+    double wg = 0.0;
+    for (int w = 0; w < kSelWaves; ++w) wg += s_red[w];
+    double total = wg;
+    if (sy.P > 1) {
+      const uint32_t tag = sy.tag_base + (uint32_t)sy.rounds + 1u;
+      uint64_t* base = sy.slot + (size_t)(sy.rounds & 1) * sy.pmax * 4;
+      if (lane < 2) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(wg);
+        const uint32_t half = lane ? (uint32_t)(bits >> 32) : (uint32_t)bits;
+        store_coherent(base + sy.w * 4 + lane, ((uint64_t)tag << 32) | half);
+      }
+      // lane i < P reads workgroup i's two words
+      uint64_t lo = 0, hi = 0;
+      bool ok = lane >= sy.P;
+      int spins = 0;
+      while (!ok) {
+        lo = load_coherent(base + lane * 4);
+        hi = load_coherent(base + lane * 4 + 1);
+        ok = (uint32_t)(lo >> 32) == tag && (uint32_t)(hi >> 32) == tag;
+        if (!ok && ++spins > (1 << 22)) {
+          raise_status(sy.status, SPEC_DEV_SYNC_TIMEOUT);
+          break;
+        }
+      }
+      const double mine =
+          lane < sy.P ? __longlong_as_double((long long)(((hi & 0xffffffffull) << 32) | (lo & 0xffffffffull)))
+                      : 0.0;
+      total = wave_sum_f64(mine);
+    }
+    if (lane == 0) {
+      *out = total;
+      *inv_out = 1.0 / total;
+    }
+  }
+  __syncthreads();
+  ++sy.rounds;
+  return *out;
+}
 
 // One row pair (target row of node s and its draft row) with its statistics.
 struct RowPair {
@@ -749,28 +813,28 @@ __device__ __forceinline__ void cache_load(RowCache& c, RowPair& rp, bool with_q
   __syncthreads();
 }
 
-// sum over the vocabulary of max(0, r - q), the next residual's normaliser
-__device__ __forceinline__ double cache_residual_mass(const RowCache& c, SeqSync& sy, SelShared& sh) {
+// this thread's part of sum max(0, r - q)
+__device__ inline double cache_mass_local(const RowCache& c) {
   double a = 0.0;
 #pragma unroll
   for (int e = 0; e < kCacheE; ++e) {
     const double w = c.r[e] - c.q[e];
     if (w > 0.0) a += w;
   }
-  a = block_sum_f64(a, sh.red);
-  sy.exchange(a, 0.0, sh.slots);
-  const double t = slot_sum(sh.slots, sy.P);
-  __syncthreads();
-  return t;
+  return a;
 }
 
-// one rejection: r <- max(0, r - q) / N
-__device__ inline void cache_residual_step(RowCache& c, double invN) {
+// one rejection and this thread's part of the next residual's mass, in one pass
+__device__ inline double cache_step_mass(RowCache& c, double invN) {
+  double a = 0.0;
 #pragma unroll
   for (int e = 0; e < kCacheE; ++e) {
     const double w = c.r[e] - c.q[e];
     c.r[e] = w > 0.0 ? w * invN : 0.0;
+    const double w2 = c.r[e] - c.q[e];
+    if (w2 > 0.0) a += w2;
   }
+  return a;
 }
 
 __device__ inline double cache_weight(const RowCache& c, int e, bool resid) {
@@ -889,6 +953,7 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
     own_lq = rp.lq[sh.tok[tid]];
   }
   bool own_stored = false;
+  double mass_next = 0.0;  // cached path: this thread's part of the next residual mass
   int remaining = sh.nch[s];
   for (int ch = s + 1; ch < T && remaining > 0; ++ch) {
     if (sh.par[ch] != s) continue;
@@ -921,6 +986,7 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
       if (A.cache) {
         cache_load(rc, rp, true, true, sy, sh);
         cached = true;
+        mass_next = cache_mass_local(rc);
       } else {
         pass_normalisers(rp, true, sy, sh, V);
       }
@@ -939,15 +1005,20 @@ __device__ __forceinline__ bool test_children_seq(const SelArgs& A, size_t nb, i
       draw_k = k;
       break;
     }
-    const double N =
-        A.cache ? cache_residual_mass(rc, sy, sh) : pass_residual_mass(rp, k, invN, sy, sh, V);
+    // cached: one exchange per rejection (it also leaves 1 / N in invN[k]),
+    // then the residual step and the next mass in one pass over the cache
+    const double N = A.cache ? reduce_exchange(sy, mass_next, sh.red, &sh.xsum, &sh.invN[k])
+                             : pass_residual_mass(rp, k, invN, sy, sh, V);
     if (!(N > 0.0) || k >= 63) {
       dead = true;
       if (tid == 0) raise_status(A.status, SPEC_DEV_RESIDUAL_ZERO);
     } else {
-      if (tid == 0) sh.invN[k] = 1.0 / N;
-      if (A.cache) cache_residual_step(rc, 1.0 / N);
-      __syncthreads();
+      if (A.cache) {
+        mass_next = cache_step_mass(rc, sh.invN[k]);
+      } else {
+        if (tid == 0) sh.invN[k] = 1.0 / N;
+        __syncthreads();
+      }
       ++k;
     }
   }
@@ -1708,30 +1779,28 @@ __global__ __launch_bounds__(kSelThreads) void k_vrwalk(SelArgs A) {
   }
 }
 
-// Largest P with B * P co-resident select workgroups, at most kMaxP, and at
-// least 2048 vocabulary entries per workgroup.
+// Largest P with B * P co-resident select workgroups (the occupancy of the
+// mode's own kernel), at most kMaxP, and at least 2048 vocabulary entries per
+// workgroup.
 int choose_p(int mode, int B, int V) {
   if (mode == SPEC_GREEDY) return 1;
-  thread_local int cached_capacity = -1;  // per host thread: no shared state
-  thread_local int cached_device = -1;
+  thread_local int cached_capacity[2] = {-1, -1};  // per host thread: no shared state
+  thread_local int cached_device[2] = {-1, -1};
+  const int slot = mode == SPEC_REJECT_PATH ? 0 : 1;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 1;
-  if (cached_device != dev) {
-    int cus = 0, per_cu = 0, per_cu_path = 0;
+  if (cached_device[slot] != dev) {
+    int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 1;
-    // the fewer of the two rejection-mode kernels' resident workgroups per CU
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu, reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_RECURSIVE>),
-            kSelThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &per_cu_path, reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_PATH>),
-            kSelThreads, 0) != hipSuccess)
+    const void* fn = slot == 0 ? reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_PATH>)
+                               : reinterpret_cast<const void*>(k_vselect<SPEC_REJECT_RECURSIVE>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kSelThreads, 0) != hipSuccess)
       return 1;
-    cached_capacity = cus * std::min(per_cu, per_cu_path);
-    cached_device = dev;
+    cached_capacity[slot] = cus * per_cu;
+    cached_device[slot] = dev;
   }
-  int P = cached_capacity / (B > 0 ? B : 1);
+  int P = cached_capacity[slot] / (B > 0 ? B : 1);
   const int by_v = V / 2048;
   if (P > by_v) P = by_v;
   if (P > kMaxP) P = kMaxP;
