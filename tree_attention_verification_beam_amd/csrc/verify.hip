@@ -82,13 +82,13 @@ VerifyPlan make_plan(int mode, int B, int T_cap, int V, int R) {
   VerifyPlan p{};
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
   p.n_units = (long)B * T_cap + (long)B * Rr;
-  p.ept = 32;
+  p.ept = 64;
   // about one workgroup per CU at least; larger chunks keep the row merges short
   while (p.ept > 4 && p.n_units * ((V + p.ept * kStatThreads - 1) / (p.ept * kStatThreads)) < 256)
     p.ept >>= 1;
   p.chunk = p.ept * kStatThreads;
   p.n_chunks = (V + p.chunk - 1) / p.chunk;
-  while (p.n_chunks > kMergeEntries && p.ept < 32) {  // very large vocabularies
+  while (p.n_chunks > kMergeEntries && p.ept < 64) {  // very large vocabularies
     p.ept <<= 1;
     p.chunk = p.ept * kStatThreads;
     p.n_chunks = (V + p.chunk - 1) / p.chunk;
@@ -1963,6 +1963,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
 #define SPEC_STATS(E)                                                                       \
   launch_stats<E>(pl, vec, B, T_cap, V, Rr, tgt, dft, n_nodes, parent, dft_row, part, sync, s)
   switch (pl.ept) {
+    case 64: SPEC_STATS(64); break;
     case 32: SPEC_STATS(32); break;
     case 16: SPEC_STATS(16); break;
     case 8: SPEC_STATS(8); break;
