@@ -210,7 +210,7 @@ int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int D, int cac
  * ws: spec_verify_workspace_size() bytes, no initial contents needed.  Calls
  * that overlap in time must not share a workspace.  The workspace size is 0
  * (and the call returns SPEC_ERR_UNSUPPORTED) for a vocabulary beyond what
- * the row merge stages: more than 1024 chunks of 8192 entries (V > 8388608)
+ * the row merge stages: more than 1024 chunks of 16384 entries (V > 16777216)
  * in the one-pass modes, V * 4 >= 2^31 in SPEC_GREEDY_WALK.
  */
 size_t spec_verify_workspace_size(int mode, int B, int T_cap, int V, int R);

@@ -117,11 +117,11 @@ def test_attention_rejects_a_row_block_beyond_32_bit_ranges(lib):
 
 def test_verify_refuses_a_vocabulary_beyond_the_row_merge(lib):
     """The one-pass verify merges a row's chunk partials in LDS batches of 1024
-    chunks of at most 8192 entries: a larger vocabulary is refused on the host
+    chunks of at most 16384 entries: a larger vocabulary is refused on the host
     (workspace size 0, SPEC_ERR_UNSUPPORTED) before anything is launched."""
     cdll = lib.load()
-    big = 32 * 256 * 1024 + 1
-    assert cdll.spec_verify_workspace_size(0, 1, 17, 32 * 256 * 1024, 0) > 0
+    big = 64 * 256 * 1024 + 1
+    assert cdll.spec_verify_workspace_size(0, 1, 17, 64 * 256 * 1024, 0) > 0
     for mode in (0, 1, 2):
         assert cdll.spec_verify_workspace_size(mode, 1, 17, big, 4) == 0
         assert cdll.spec_verify(mode, 1, 17, big, 4, *([16] * 17), 1 << 30, None, None) == -2

@@ -1950,7 +1950,7 @@ extern "C" int spec_verify(int mode, int B, int T_cap, int V, int R, const float
   }
   const VerifyPlan pl = make_plan(mode, B, T_cap, V, R);
   // a row's chunk partials are merged in LDS batches of kMergeEntries: a
-  // vocabulary with more chunks than that (V > 32 * 256 * 1024) is refused
+  // vocabulary with more chunks than that (V > 64 * 256 * 1024) is refused
   if (pl.n_chunks > kMergeEntries) return SPEC_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < pl.total || !aligned(ws, 256)) return SPEC_ERR_WORKSPACE;
   const int Rr = mode == SPEC_GREEDY ? 0 : R;
