@@ -43,3 +43,23 @@ def test_attention_split_counts(gpu, case):
     attn_bar(res["attn"], ref, case)
     for b in range(B):
         assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)
+
+
+def test_gqa_row_blocks_every_row(gpu):
+    """The 70B-class GQA plan without context splits (16 sequences, 64 query
+    heads on 8 KV heads, 16 beams of 4: up to 65 nodes, five 128-row blocks per
+    (sequence, KV head) reading one key range), every row of every sequence
+    against the oracle, with ragged contexts."""
+    B, H, Hkv = 16, 64, 8
+    ctx = [200 + 23 * i for i in range(B)]
+    inp = synth.make_custom_inputs(9200, B=B, H=H, Hkv=Hkv, D=128, V=500, dtype="bf16",
+                                   ctx_lens=ctx, tree="beams", W=16, L=4)
+    log(f"case GQA row blocks: B={B} H={H} Hkv={Hkv} T_cap={inp['T_cap']} ctx={ctx[0]}..{ctx[-1]}")
+    tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+    res = pipeline.Step(inp, "greedy").run(compact=False)
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    attn_bar(res["attn"], ref, "GQA row blocks")
+    for b in range(B):
+        assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)
