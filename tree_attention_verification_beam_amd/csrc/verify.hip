@@ -191,16 +191,24 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
         store_coherent(reinterpret_cast<uint64_t*>(sync + (size_t)b * kSyncStride) + i, 0);
     row = tgt + unit * (long)V;
   } else {
-    // a draft row is needed iff it is the draft row of some node with a child
+    // a draft row is needed iff it is the draft row of some node with a child;
+    // the node count, parents and draft rows are read in one round trip and
+    // the parents' rows looked up in LDS
     const long u2 = unit - n_tgt;
     const int b = (int)(u2 / Rr), r = (int)(u2 - (long)b * Rr);
-    if (tid == 0) s_need = 0;
-    __syncthreads();
-    const int T = min(n_nodes[b], T_cap);
-    for (int u = 1 + tid; u < T; u += kStatThreads) {
-      const int p = parent[(size_t)b * T_cap + u];
-      if (p >= 0 && p < u && dft_row[(size_t)b * T_cap + p] == r) s_need = 1;
+    __shared__ int s_row[SPEC_MAX_TREE];
+    static_assert(kStatThreads >= SPEC_MAX_TREE, "one tree row per thread");
+    const int T_n = n_nodes[b];
+    int my_par = -1, my_row = -1;
+    if (tid < T_cap) {
+      my_par = parent[(size_t)b * T_cap + tid];
+      my_row = dft_row[(size_t)b * T_cap + tid];
     }
+    if (tid == 0) s_need = 0;
+    if (tid < T_cap) s_row[tid] = my_row;
+    __syncthreads();
+    const int T = min(T_n, T_cap);
+    if (tid >= 1 && tid < T && my_par >= 0 && my_par < tid && s_row[my_par] == r) s_need = 1;
     __syncthreads();
     if (!s_need) return;
     row = dft + u2 * (long)V;
