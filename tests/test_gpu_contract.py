@@ -5,7 +5,8 @@
 - spec_kv_compact on paths of up to 127 nodes (a workgroup's LDS buffer
   full), against the oracle, with its arrival counters back at zero;
 - the greedy walk and the one-pass verify on workspaces filled with arbitrary
-  bytes before the first call (no initial contents are needed).
+  bytes before the first call (no initial contents are needed);
+- the bandwidth probes read (and copy) exactly their buffers.
 """
 import numpy as np
 import pytest
@@ -133,3 +134,21 @@ def test_verify_on_a_workspace_of_arbitrary_bytes(gpu, mode):
         res = st.run()
         assert res["status"] == 0, sv.decode_status(res["status"])
         assert_verify_equal(res, ref, f"{mode} arbitrary workspace call {rep}")
+
+
+@pytest.mark.parametrize("n_bytes,n_blocks", [(3 * (256 << 10) + 4096 + 48, 2), (256 << 10, 8), (16, 1)])
+def test_read_probe_reads_every_byte_once(gpu, n_bytes, n_blocks):
+    """The bandwidth probes read exactly their buffer: the streaming read's
+    per-workgroup sums over a buffer of fp32 twos (whole 256 KiB chunks, a
+    partial last chunk, fewer workgroups than chunks) add up to 2 * n_bytes / 4;
+    the copy reproduces its source."""
+    log(f"case read probe n_bytes={n_bytes} blocks={n_blocks}")
+    src = torch.full((n_bytes // 4,), 2.0, dtype=torch.float32, device="cuda")
+    out = torch.full((n_blocks,), -1.0, dtype=torch.float32, device="cuda")
+    sv.spec_read_probe(src, n_bytes, out, n_blocks)
+    torch.cuda.synchronize()
+    assert float(out.double().sum()) == 2.0 * (n_bytes // 4)
+    dst = torch.zeros_like(src)
+    sv.spec_copy_probe(src, dst, n_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
