@@ -3,9 +3,11 @@
 The context of a (sequence, KV head) is split over workgroups so that the grid
 covers the CUs; a merge kernel then combines the (max, sum, O) partials.  The
 shapes below make the plan choose 1, 2, 4, 21 and 32 splits (the last two with
-two and with one key group) and, for 1024 (sequence, head) streams, 4-wave
-groups; each is compared with the oracle within 1e-2 of the largest output,
-with ragged contexts where B > 1.
+two and with one key group), for 1024 (sequence, head) streams 4-wave groups,
+and 24 splits of the 4-wave GQA plan that loads its tiles straight into LDS;
+each is compared with the oracle within 1e-2 of the largest output, with
+ragged contexts where B > 1.  The same GQA plan is also run without splits on
+the 70B shape and on ranges shorter than one key tile.
 """
 import numpy as np
 import pytest
@@ -26,6 +28,8 @@ CASES = {
     "32 splits, GQA": (1, 4, 1, [8000]),
     # 1024 (sequence, head) streams of at most 32 rows: 4-wave groups
     "1024 streams": (32, 32, 32, [40 + 7 * i for i in range(32)]),
+    # 272 rows per KV head: the 4-wave plan whose tiles go straight to LDS
+    "24 splits, GQA direct loads": (1, 32, 2, [3000]),
 }
 
 
@@ -61,5 +65,34 @@ def test_gqa_row_blocks_every_row(gpu):
     ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
                                 tr["anc"])
     attn_bar(res["attn"], ref, "GQA row blocks")
+    for b in range(B):
+        assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)
+
+
+def test_gqa_direct_loads_short_ranges(gpu):
+    """The direct-to-LDS GQA plan (16 query heads per KV head, 17 nodes: 272
+    rows, three row blocks) on key ranges that end inside the first tile (no
+    context, 5 context keys: the first tile is loaded over every cache slot
+    and its rows past the range are zeroed in LDS) and inside the second tile
+    (the loads' range check returns zeros), against the oracle; the cache
+    slots past each sequence's keys hold NaN."""
+    B, H, Hkv = 4, 32, 2
+    ctx = [0, 5, 64, 130]
+    inp = synth.make_custom_inputs(9300, B=B, H=H, Hkv=Hkv, D=128, V=500, dtype="bf16",
+                                   ctx_lens=ctx, tree="beams", W=4, L=4)
+    log(f"case GQA direct loads: B={B} H={H} Hkv={Hkv} T_cap={inp['T_cap']} ctx={ctx}")
+    assert (H // Hkv) * inp["T_cap"] > 256
+    tr = oracle.build_tree_beams(inp["beams"], inp["root_token"], inp["T_cap"])
+    # cache slots past each sequence's keys hold NaN: none may reach an output
+    assert inp["k"].dtype == np.uint16
+    for b in range(B):
+        end = ctx[b] + int(tr["n_nodes"][b])
+        inp["k"][b, :, end:] = 0x7FC0
+        inp["v"][b, :, end:] = 0x7FC0
+    res = pipeline.Step(inp, "greedy").run(compact=False)
+    assert res["status"] == 0, gpu.decode_status(res["status"])
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    attn_bar(res["attn"], ref, "GQA direct loads")
     for b in range(B):
         assert np.all(res["attn"][b, tr["n_nodes"][b]:] == 0)

@@ -5,7 +5,8 @@
 // Domain: every first-tile-key offset nctx = ctx - kt0 in [-140, 80] and range
 // end nin = k_end - kt0 in [-4, 80], ancestor words of many shapes (random,
 // single bits at 0, 63, 64, 127, chains, all ones, none), every lane group lg
-// in 0..3 and wave key offset wkey0 in {0, 32}.  For each case every tile key
+// in 0..3, wave key offset wkey0 in {0, 32} and both key orders (the staged
+// layout's and the direct-load layout's).  For each case every tile key
 // p in 0..63 and every lane bit is compared with the definition: key kt0 + p is
 // visible iff it lies inside the range and is a context key or a tree key
 // whose ancestor bit is set.
@@ -99,6 +100,21 @@ int main() {
                   ++checked;
                 }
           }
+        }
+        for (int lg = 0; lg < 4; ++lg) {
+          // direct-load layout: natural key order over the whole tile
+          const uint64_t lv = spec::lane_vis_bits_direct(bits, lg);
+          for (int j = 0; j < 2; ++j)
+            for (int st = 0; st < 2; ++st)
+              for (int e = 0; e < 4; ++e) {
+                const int key = 32 * j + 8 * lg + 4 * st + e;
+                const int c = 32 * j + 4 * st + e;
+                if ((((lv >> c) & 1ull) != 0) != brute(key, nctx, nin, m0, m1)) {
+                  std::printf("direct lane bit mismatch: nctx %d nin %d lg %d c %d\n", nctx, nin, lg, c);
+                  return 1;
+                }
+                ++checked;
+              }
         }
       }
     }

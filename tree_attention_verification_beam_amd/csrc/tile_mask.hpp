@@ -51,4 +51,11 @@ SPEC_HD inline uint64_t lane_vis_bits(uint64_t tile_bits, int wkey0, int lg) {
   return ((lg >> 1) & 1) ? sw : v;
 }
 
+// The same for the direct-load layout (one key group over the whole tile,
+// keys in natural order): the lane group lg holds keys 32 j + 8 lg + 4 st + e,
+// and bit 32 j + 4 st + e of the result is that key's visibility.
+SPEC_HD inline uint64_t lane_vis_bits_direct(uint64_t tile_bits, int lg) {
+  return tile_bits >> (8 * lg);
+}
+
 }  // namespace spec

@@ -50,6 +50,7 @@ struct AttnPlan {
   int QT;        // 16-row query tiles per wave
   int KG;        // key groups (waves splitting one key tile)
   int PF;        // tiles of global loads in flight per workgroup (1 or 2)
+  int NS;        // LDS stages of direct-to-LDS tile loads (0: tiles staged through registers)
   int n_mt;      // row blocks (workgroups sharing one key range)
   int n_splits;  // context splits
   int tiles_per_split;
@@ -74,7 +75,7 @@ void finish_plan(AttnPlan& p, int B, int T_cap, int H, int Hkv, int max_ctx, int
 // Shape-driven choice of the tiling: enough query tiles per wave to reuse each
 // K/V tile across the whole G*T row block, and enough context splits that the
 // busy workgroups cover every CU about once (or twice for 4-wave groups).
-AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
+AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int D, int max_ctx) {
   AttnPlan p{};
   const int nq = (H / Hkv * T_cap + 15) / 16;
   p.NW = 8;
@@ -90,9 +91,11 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int max_ctx) {
     p.KG = 1; p.QT = 2; p.PF = 2;
   } else {
     // many rows (wide GQA groups): 128-row blocks of 4 waves with two query
-    // tiles each read the same key range, two workgroups per CU, two tiles of
-    // loads in flight
+    // tiles each read the same key range, two workgroups per CU; at D = 128
+    // the tiles go straight to LDS (two stages), which frees the staging
+    // registers and the stores from the waves
     p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 2;
+    if (D == 128) p.NS = 2;
   }
   const long units = (long)B * Hkv;
   const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
@@ -148,6 +151,21 @@ struct Lds {
   static constexpr int kBytes = 2 * kStage * 2;  // two stages of bf16
 };
 
+// Direct-to-LDS layout (one key group, D = 128): a stage holds the tile's K
+// and V rows as loaded, 64 rows of 256 bytes each, K first.  A 16-byte load
+// writes lane l's bytes at slot l of a 1 KB block (four rows), so the layout
+// is row-major with no padding; instead the 16-byte chunk c of key row k sits
+// at position c ^ swz(k) of its row, swz(k) = 2 ((k & 3) | ((k >> 3) & 1) << 2).
+// With it the K operand reads (16 bytes) and the V operand reads (transposing
+// 8-byte reads of 16-bit elements) are free of bank conflicts (measured on
+// gfx950 with SQ_LDS_BANK_CONFLICT).
+struct LdsDirect {
+  static constexpr int kRow = 256;                 // bytes per key row
+  static constexpr int kStageK = kKeyTile * kRow;  // 16 KB
+  static constexpr int kStage = 2 * kStageK;       // K + V
+  static __device__ constexpr int swz(int key) { return ((key & 3) << 1) | (((key >> 3) & 1) << 3); }
+};
+
 struct AttnArgs {
   int B, T_cap, H, Hkv, cache_cap, max_ctx, n_splits, tiles_per_split, n_kv, n_mt;
   float scale_log2;
@@ -174,6 +192,35 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until at most N vector memory operations of this wave are outstanding
+// (loads into LDS complete in issue order).
+template <int N>
+__device__ inline void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One 16-byte-per-lane load into LDS: lane l's bytes land at LDS byte address
+// lds + 16 l; the buffer resource's range check returns zeros past its end.
+// Written in assembly so that the compiler's wait insertion does not take the
+// loads for pending writes to all of LDS (it would then wait for them before
+// every transposing read): the kernel waits for them itself (wait_loads)
+// before the barrier that hands a stage over.  M0 carries the LDS address and
+// is restored; the leading s_nop covers a VALU write of the resource's SGPRs
+// (5 wait states), the one after the M0 write the LDS-DMA hazard.
+template <bool NT>
+__device__ inline void load_lds_b128(u32x4 rsrc, unsigned lds, int voffset) {
+  unsigned saved;
+  if constexpr (NT)
+    asm volatile("s_nop 4\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen nt lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+  else
+    asm volatile("s_nop 4\n\ts_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "s"(lds), "v"(voffset), "s"(rsrc) : "memory");
+}
+
 // Map a workgroup slot to (kv unit, row block) so that the row blocks sharing
 // one key stream land on the same XCD (slots are dealt round-robin over 8 XCDs).
 __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
@@ -183,9 +230,11 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
-template <int D, int NW, int QT, int KG, int PF, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   constexpr int kThreads = NW * 64;
+  constexpr bool DL = NS > 0;  // direct-to-LDS tile loads
+  static_assert(!DL || (KG == 1 && D == 128 && NS >= 2 && NS <= 4), "direct-load plans");
   constexpr int RG = NW / KG;           // row groups
   constexpr int KSTEPS = D / 32;        // k-steps of Q K^T
   constexpr int DT = D / 16;            // 16-wide d tiles of the output
@@ -286,8 +335,44 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       if (kt0 + VK * kq + j > last) vr[j] = bf16x8{};
   };
 
-  bf16x8 kA[K_UNITS], vA[VK];
-  load_tile(kA, vA, k_begin, a.cache_cap);  // every cache slot: sanitized below
+  // Direct-to-LDS loads: the tile's K (and V) rows form 16 blocks of 1 KB
+  // (four rows); wave w issues blocks w, w + NW, ...  Lane l of a block loads
+  // the chunk that belongs at slot l (row 4 R + l / 16, position l % 16), so
+  // the swizzle costs nothing; every voffset is fixed per thread.
+  constexpr int DL_BLOCKS = DL ? kKeyTile * LdsDirect::kRow / 1024 / NW : 1;  // per wave, K or V
+  constexpr int DL_LOADS = 2 * DL_BLOCKS;                                      // per thread and tile
+  int dl_off[DL_BLOCKS];
+  if constexpr (DL) {
+#pragma unroll
+    for (int u = 0; u < DL_BLOCKS; ++u) {
+      const int row = 4 * (u * NW + wave) + (lane >> 4);
+      dl_off[u] = row * LdsDirect::kRow + 16 * ((lane & 15) ^ LdsDirect::swz(row));
+    }
+  }
+  const unsigned lds0 = (unsigned)(size_t)((__attribute__((address_space(3))) unsigned char*)smem_raw);
+  auto rsrc_words = [&](const bf16_t* base, int kt0, int limit) {
+    const int rows = limit - kt0 > 0 ? limit - kt0 : 0;
+    const unsigned long long addr = (unsigned long long)(base + (size_t)kt0 * D);
+    return u32x4{(unsigned)addr, (unsigned)(addr >> 32) & 0xffffu, (unsigned)(rows * kRowBytes),
+                 (unsigned)kBufferWord3};
+  };
+  auto issue_tile = [&](int stage, int kt0, int limit) {
+    const u32x4 rk = rsrc_words(kbase, kt0, limit);
+    const u32x4 rv = rsrc_words(vbase, kt0, limit);
+    const unsigned st = lds0 + stage * LdsDirect::kStage;
+#pragma unroll
+    for (int u = 0; u < DL_BLOCKS; ++u) {
+      const unsigned blk = st + (u * NW + wave) * 1024;
+      load_lds_b128<ONCE>(rk, blk, dl_off[u]);
+      load_lds_b128<ONCE>(rv, blk + LdsDirect::kStageK, dl_off[u]);
+    }
+  };
+
+  bf16x8 kA[DL ? 1 : K_UNITS], vA[DL ? 1 : VK];
+  if constexpr (DL)
+    issue_tile(0, k_begin, a.cache_cap);  // every cache slot: rows past the range zeroed below
+  else
+    load_tile(kA, vA, k_begin, a.cache_cap);  // every cache slot: sanitized below
 
   // Q fragments: B operand of S^T = K Q^T; lane (query l16, group lg) holds
   // Q[row][32s + 8lg .. +8]
@@ -353,10 +438,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         a.part_l[ubase + r] = 0.0f;
       }
     }
+    if constexpr (DL) wait_loads<0>();  // no load into LDS outlives the workgroup
     return;
   }
   const int klast = k_end - 1;
-  sanitize_tile(kA, vA, k_begin, klast);
+  if constexpr (!DL) sanitize_tile(kA, vA, k_begin, klast);
 
   // ---------------------------------------------------------------- state
   f32x4 acc[QT][DT];
@@ -415,9 +501,31 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     return tile_vis_bits(ctx - kt0, k_end - kt0, mask0[i], mask1[i]);
   };
 
+  // Direct-load operand addresses (bytes inside a stage).  K: lane (l16, lg)
+  // reads key 32 j + 8 q + 4 st + r (q = l16 / 4, r = l16 % 4) at chunk
+  // 4 s + lg.  V^T: each transposing read covers 16 rows of 4 elements per
+  // 16-lane group; lane r of group lg names row (key 32 j + 8 lg + 4 hf + r / 4,
+  // dims 16 dt + 4 (r % 4) .. + 3), and lane m of the group receives the four
+  // keys' values of dim 16 dt + m, that is elements 4 hf .. 4 hf + 3 of its
+  // V^T operand.
+  int dl_k[DL ? KSTEPS : 1], dl_v[DL ? DT : 1];
+  if constexpr (DL) {
+    const int q = l16 >> 2, r = l16 & 3;
+    const int swk = LdsDirect::swz(8 * q + r);
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) dl_k[s] = (8 * q + r) * LdsDirect::kRow + 16 * ((4 * s + lg) ^ swk);
+    const int ra = l16 & 3, rk = l16 >> 2;
+    const int s2 = LdsDirect::swz(8 * lg + rk) >> 1;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      dl_v[dt] = LdsDirect::kStageK + (8 * lg + rk) * LdsDirect::kRow + 32 * (dt ^ s2) + 8 * ra;
+  }
+
   auto compute_tile = [&](int stage, int kt0) {
-    const bf16_t* sk = smem + stage * Lds<D>::kStage;
+    const bf16_t* sk = smem + stage * (DL ? LdsDirect::kStage / 2 : Lds<D>::kStage);
     const bf16_t* sv = sk + Lds<D>::kStageK;
+    const unsigned char* sb = smem_raw + stage * LdsDirect::kStage;
+    (void)sv; (void)sb;
     if (!wave_on) return;  // no live query tile in this wave (uniform)
     const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
     // this lane's keys of chunk j are wkey0 + 32 j + 8 lg + 4 (st ^ h) + e
@@ -425,7 +533,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     uint64_t lvis[QT];
     if (need_mask) {
 #pragma unroll
-      for (int i = 0; i < QT; ++i) lvis[i] = lane_vis_bits(tile_vis(i, kt0), wkey0, lg);
+      for (int i = 0; i < QT; ++i)
+        lvis[i] = DL ? lane_vis_bits_direct(tile_vis(i, kt0), lg) : lane_vis_bits(tile_vis(i, kt0), wkey0, lg);
     }
     // Scores of all this wave's keys of the tile first, then one online-softmax
     // step over them (one maximum check and rescale per tile), then P V: the
@@ -437,11 +546,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bf16x8 kf[KSTEPS];
-        const int q = l16 >> 2;
-        const int kk = ck0 + 8 * q + 4 * (st ^ ((q >> 1) & 1)) + (l16 & 3);  // this lane's key row
-        const bf16_t* krow = sk + kk * Lds<D>::kPitchK + 8 * lg;
+        if constexpr (DL) {
 #pragma unroll
-        for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
+          for (int s = 0; s < KSTEPS; ++s)
+            kf[s] = *reinterpret_cast<const bf16x8*>(sb + dl_k[s] + ck0 * LdsDirect::kRow + st * 4 * LdsDirect::kRow);
+        } else {
+          const int q = l16 >> 2;
+          const int kk = ck0 + 8 * q + 4 * (st ^ ((q >> 1) & 1)) + (l16 & 3);  // this lane's key row
+          const bf16_t* krow = sk + kk * Lds<D>::kPitchK + 8 * lg;
+#pragma unroll
+          for (int s = 0; s < KSTEPS; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(krow + 32 * s);
+        }
 #pragma unroll
         for (int i = 0; i < QT; ++i) {
           // a dead tile of a live wave has zero Q: its scores are computed
@@ -520,9 +635,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       const int ck0 = wkey0 + 32 * j;
 #pragma unroll
       for (int d = 0; d < DT; ++d) {
-        const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
-        const int sw = Lds<D>::swz(16 * d);  // the same for rows 16d .. 16d+15
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + ((ck0 + 8 * lg) ^ sw));
+        bf16x8 vf;
+        if constexpr (DL) {
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const unsigned char* vp = sb + dl_v[d] + ck0 * LdsDirect::kRow;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vp + 4 * LdsDirect::kRow));
+          vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          const bf16_t* vrow = sv + (16 * d + l16) * Lds<D>::kPitchV;
+          const int sw = Lds<D>::swz(16 * d);  // the same for rows 16d .. 16d+15
+          vf = *reinterpret_cast<const bf16x8*>(vrow + ((ck0 + 8 * lg) ^ sw));
+        }
 #pragma unroll
         for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[j][i], acc[i][d]);
       }
@@ -537,7 +661,37 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // LDS double buffer; PF tiles of global loads in flight.  The barrier waits
   // for this wave's LDS traffic only, so prefetched global loads stay in flight.
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
-  if constexpr (PF == 1) {
+  if constexpr (DL) {
+    // NS stages: tile it lives in stage it % NS.  The loads of tile it + NS - 1
+    // go into the stage tile it - 1 used, issued after the barrier that ended
+    // its reads, so NS - 1 tiles of loads are in flight during a tile's work.
+    // Loads past the range are issued too (a zero-length range fetches
+    // nothing), which keeps the wait counts fixed.
+#pragma unroll
+    for (int t = 1; t < NS - 1; ++t) issue_tile(t, k_begin + t * kKeyTile, k_end);
+    wait_loads<(NS - 2) * DL_LOADS>();  // this wave's loads of tile 0
+    if (k_begin + kKeyTile > k_end) {
+      // tile 0 was loaded over every cache slot: zero its rows past the range
+      // (cache slots past the sequence may hold any bits, NaN included)
+      lds_barrier();
+      const int n_in = k_end - k_begin;
+      for (int e = tid; e < (kKeyTile - n_in) * 32; e += kThreads) {
+        const int row = n_in + (e >> 5), part = e & 31;  // 16 chunks of K, then 16 of V
+        *reinterpret_cast<u32x4*>(smem_raw + (part >> 4) * LdsDirect::kStageK + row * LdsDirect::kRow +
+                                  16 * (part & 15)) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    lds_barrier();
+#pragma unroll 1
+    for (int it = 0; it < n_tiles; ++it) {
+      const int ahead = it + NS - 1;
+      issue_tile(ahead % NS, k_begin + ahead * kKeyTile, k_end);
+      compute_tile(it % NS, k_begin + it * kKeyTile);
+      wait_loads<(NS - 2) * DL_LOADS>();  // tile it + 1 has landed
+      lds_barrier();
+    }
+    wait_loads<0>();
+  } else if constexpr (PF == 1) {
     store_tile(kA, vA, 0);
     lds_barrier();
 #pragma unroll 1
@@ -823,10 +977,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
 
 // ------------------------------------------------------------------ launchers
 
-template <int D, int NW, int QT, int KG, int PF, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
 int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
-  auto kern = k_attn_bf16<D, NW, QT, KG, PF, ONCE>;
-  const int lds = Lds<D>::kBytes;
+  auto kern = k_attn_bf16<D, NW, QT, KG, PF, NS, ONCE>;
+  const int lds = NS > 0 ? NS * LdsDirect::kStage : Lds<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   hipLaunchKernelGGL(kern, dim3(p.n_slots), dim3(NW * 64), lds, s, args);
@@ -839,15 +993,18 @@ int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
 template <int D>
 int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   const bool once = p.n_mt == 1;
-#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_)                                \
-  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_)           \
-    return once ? launch_main<D, NW_, QT_, KG_, PF_, true>(p, args, s)    \
-                : launch_main<D, NW_, QT_, KG_, PF_, false>(p, args, s);
-  SPEC_ATTN_CASE(8, 1, 2, 1)
-  SPEC_ATTN_CASE(8, 1, 2, 2)
-  SPEC_ATTN_CASE(4, 1, 2, 2)
-  SPEC_ATTN_CASE(8, 2, 1, 2)
-  SPEC_ATTN_CASE(4, 2, 1, 2)
+#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_, NS_)                                           \
+  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_ && p.NS == NS_)            \
+    return once ? launch_main<D, NW_, QT_, KG_, PF_, NS_, true>(p, args, s)               \
+                : launch_main<D, NW_, QT_, KG_, PF_, NS_, false>(p, args, s);
+  SPEC_ATTN_CASE(8, 1, 2, 1, 0)
+  SPEC_ATTN_CASE(8, 1, 2, 2, 0)
+  SPEC_ATTN_CASE(4, 1, 2, 2, 0)
+  SPEC_ATTN_CASE(8, 2, 1, 2, 0)
+  SPEC_ATTN_CASE(4, 2, 1, 2, 0)
+  if constexpr (D == 128) {
+    SPEC_ATTN_CASE(4, 2, 1, 2, 2)
+  }
 #undef SPEC_ATTN_CASE
   return SPEC_ERR_UNSUPPORTED;
 }
@@ -922,7 +1079,7 @@ extern "C" size_t spec_tree_attention_workspace_size(int dt, int B, int T_cap, i
                                                      int D, int max_ctx) {
   if (dt != SPEC_BF16 || B < 1 || T_cap < 1 || H < 1 || Hkv < 1 || H % Hkv || max_ctx < 0)
     return 0;
-  const AttnPlan p = make_plan(B, T_cap, H, Hkv, max_ctx);
+  const AttnPlan p = make_plan(B, T_cap, H, Hkv, D, max_ctx);
   return partial_bytes(p, B, T_cap, H, Hkv, D);
 }
 
@@ -957,7 +1114,7 @@ extern "C" int spec_tree_attention(int dt, int B, int T_cap, int H, int Hkv, int
   if ((long long)cache_cap * D * 2 > 0x7fffffffLL) return SPEC_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
     return SPEC_ERR_INVALID;
-  const AttnPlan p = make_plan(B, T_cap, H, Hkv, max_ctx);
+  const AttnPlan p = make_plan(B, T_cap, H, Hkv, D, max_ctx);
   const size_t need = partial_bytes(p, B, T_cap, H, Hkv, D);
   if (need && (!ws || ws_bytes < need || !aligned(ws, 256))) return SPEC_ERR_WORKSPACE;
   return run_bf16(p, B, T_cap, H, Hkv, D, cache_cap, max_ctx, q, k_cache, v_cache, ctx_len,
