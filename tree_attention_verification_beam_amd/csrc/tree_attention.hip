@@ -15,7 +15,9 @@
 // for all of them.  A workgroup of NW waves owns a slice of those rows (QT
 // 16-row MFMA tiles per wave) and a range of keys: it streams 64-key K and V
 // tiles through LDS (double-buffered; V stored transposed so the P V operand is
-// a contiguous LDS read), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 so
+// a contiguous LDS read; for wide GQA groups at D = 128 the tiles are loaded
+// straight into LDS as they lie in memory and the V^T operand comes from
+// transposing LDS reads), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 so
 // that each lane owns one query row, runs the online softmax in fp32 in exp2
 // form, and accumulates O^T = V^T P^T with the same MFMA (and, when every wave
 // sees all keys of a tile, the row sums of P as one more MFMA against an
@@ -50,7 +52,7 @@ struct AttnPlan {
   int QT;        // 16-row query tiles per wave
   int KG;        // key groups (waves splitting one key tile)
   int PF;        // tiles of global loads in flight per workgroup (1 or 2)
-  int NS;        // LDS stages of direct-to-LDS tile loads (0: tiles staged through registers)
+  bool DL;       // direct-to-LDS tiles, scores one tile ahead (else staged through registers)
   int n_mt;      // row blocks (workgroups sharing one key range)
   int n_splits;  // context splits
   int tiles_per_split;
@@ -92,10 +94,11 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int D, int max_ctx) {
   } else {
     // many rows (wide GQA groups): 128-row blocks of 4 waves with two query
     // tiles each read the same key range, two workgroups per CU; at D = 128
-    // the tiles go straight to LDS (two stages), which frees the staging
-    // registers and the stores from the waves
+    // the tiles go straight to LDS, which frees the staging registers and the
+    // stores from the waves, and the scores of the next tile run beside the
+    // softmax and P V of this one
     p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 2;
-    if (D == 128) p.NS = 2;
+    p.DL = D == 128;
   }
   const long units = (long)B * Hkv;
   const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
@@ -230,11 +233,10 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
-template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, bool DL, bool ONCE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   constexpr int kThreads = NW * 64;
-  constexpr bool DL = NS > 0;  // direct-to-LDS tile loads
-  static_assert(!DL || (KG == 1 && D == 128 && NS >= 2 && NS <= 4), "direct-load plans");
+  static_assert(!DL || (KG == 1 && D == 128), "direct-load plans: one key group, D = 128");
   constexpr int RG = NW / KG;           // row groups
   constexpr int KSTEPS = D / 32;        // k-steps of Q K^T
   constexpr int DT = D / 16;            // 16-wide d tiles of the output
@@ -340,7 +342,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // the chunk that belongs at slot l (row 4 R + l / 16, position l % 16), so
   // the swizzle costs nothing; every voffset is fixed per thread.
   constexpr int DL_BLOCKS = DL ? kKeyTile * LdsDirect::kRow / 1024 / NW : 1;  // per wave, K or V
-  constexpr int DL_LOADS = 2 * DL_BLOCKS;                                      // per thread and tile
   int dl_off[DL_BLOCKS];
   if constexpr (DL) {
 #pragma unroll
@@ -366,6 +367,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       load_lds_b128<ONCE>(rk, blk, dl_off[u]);
       load_lds_b128<ONCE>(rv, blk + LdsDirect::kStageK, dl_off[u]);
     }
+  };
+  // K or V rows alone (the pipelined loop keeps K one tile ahead of V)
+  auto issue_rows = [&](const bf16_t* base, int stage, bool v_part, int kt0, int limit) {
+    const u32x4 rs = rsrc_words(base, kt0, limit);
+    const unsigned st = lds0 + stage * LdsDirect::kStage + (v_part ? LdsDirect::kStageK : 0);
+#pragma unroll
+    for (int u = 0; u < DL_BLOCKS; ++u) load_lds_b128<ONCE>(rs, st + (u * NW + wave) * 1024, dl_off[u]);
   };
 
   bf16x8 kA[DL ? 1 : K_UNITS], vA[DL ? 1 : VK];
@@ -521,25 +529,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       dl_v[dt] = LdsDirect::kStageK + (8 * lg + rk) * LdsDirect::kRow + 32 * (dt ^ s2) + 8 * ra;
   }
 
-  auto compute_tile = [&](int stage, int kt0) {
-    const bf16_t* sk = smem + stage * (DL ? LdsDirect::kStage / 2 : Lds<D>::kStage);
-    const bf16_t* sv = sk + Lds<D>::kStageK;
+  // One 64-key tile in three phases: the scores S^T = K Q^T of all this
+  // wave's keys of the tile (per 32-key chunk j, two 16-key sub-tiles st), one
+  // online-softmax step over them (one maximum check and rescale per tile),
+  // then O^T += V^T P^T with each chunk as one 32-key k-step.  The pipelined
+  // loop below runs the scores of the next tile beside the softmax and P V of
+  // this one.
+  typedef f32x4 Scores[PV_STEPS][QT][2];
+  typedef bf16x8 Probs[PV_STEPS][QT];
+  // K of the tile in LDS stage `stage`
+  auto tile_scores = [&](int stage, Scores& sacc) {
+    const bf16_t* sk = smem + stage * Lds<D>::kStage;
     const unsigned char* sb = smem_raw + stage * LdsDirect::kStage;
-    (void)sv; (void)sb;
-    if (!wave_on) return;  // no live query tile in this wave (uniform)
-    const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
-    // this lane's keys of chunk j are wkey0 + 32 j + 8 lg + 4 (st ^ h) + e
-    // (h = (lg >> 1) & 1); bit 32 j + 4 st + e of lvis[i] is that key's
-    uint64_t lvis[QT];
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < QT; ++i)
-        lvis[i] = DL ? lane_vis_bits_direct(tile_vis(i, kt0), lg) : lane_vis_bits(tile_vis(i, kt0), wkey0, lg);
-    }
-    // Scores of all this wave's keys of the tile first, then one online-softmax
-    // step over them (one maximum check and rescale per tile), then P V: the
-    // MFMA work of the tile comes in two blocks with the VALU work between.
-    f32x4 sacc[PV_STEPS][QT][2];
+    (void)sk; (void)sb;
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
       const int ck0 = wkey0 + 32 * j;  // first key of the chunk inside the tile
@@ -568,9 +570,20 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         }
       }
     }
+  };
 
-    // keys past the range or outside the node's ancestor set score -inf
+  // the tile's first key is kt0
+  auto tile_softmax = [&](int kt0, Scores& sacc, Probs& pf) {
+    const bool need_mask = kt0 + kKeyTile > ctx || kt0 + kKeyTile > k_end;
+    // keys past the range or outside the node's ancestor set score -inf; this
+    // lane's keys of chunk j are wkey0 + 32 j + 8 lg + 4 (st ^ h) + e (h = 0
+    // for the direct-load layout, else (lg >> 1) & 1); bit 32 j + 4 st + e of
+    // lvis[i] is that key's
     if (need_mask) {
+      uint64_t lvis[QT];
+#pragma unroll
+      for (int i = 0; i < QT; ++i)
+        lvis[i] = DL ? lane_vis_bits_direct(tile_vis(i, kt0), lg) : lane_vis_bits(tile_vis(i, kt0), wkey0, lg);
 #pragma unroll
       for (int j = 0; j < PV_STEPS; ++j)
 #pragma unroll
@@ -587,23 +600,33 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     }
 
     // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
-    // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e
-    bf16x8 pf[PV_STEPS][QT];
+    // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e.  A row maximum moves only when some
+    // lane outgrew it by 2^kRescale; then the 4 lane groups holding the row
+    // agree on the new maximum.  One uniform branch covers every query tile's
+    // rescale, so the exponentials of all tiles share one basic block with
+    // whatever MFMA work follows.
+    float lmax[QT];
+    bool grow[QT];
+    bool any_grow = false;
 #pragma unroll
     for (int i = 0; i < QT; ++i) {
-      float lmax = -INFINITY;
+      lmax[i] = -INFINITY;
 #pragma unroll
       for (int j = 0; j < PV_STEPS; ++j)
-        lmax = fmaxf(lmax, fmaxf(fmaxf(fmaxf(sacc[j][i][0][0], sacc[j][i][0][1]),
-                                       fmaxf(sacc[j][i][0][2], sacc[j][i][0][3])),
-                                 fmaxf(fmaxf(sacc[j][i][1][0], sacc[j][i][1][1]),
-                                       fmaxf(sacc[j][i][1][2], sacc[j][i][1][3]))));
-      lmax *= c;
-      // the row maximum moves only when some lane outgrew it by 2^kRescale;
-      // then the 4 lane groups holding the row agree on the new maximum
-      if (__builtin_amdgcn_ballot_w64(lmax > m_run[i] + kRescale) != 0ull) {
-        float tmax = fmaxf(lmax, partner_f32<4>(lmax));  // lane l ^ 16
-        tmax = fmaxf(tmax, partner_f32<5>(tmax));        // lane l ^ 32
+        lmax[i] = fmaxf(lmax[i], fmaxf(fmaxf(fmaxf(sacc[j][i][0][0], sacc[j][i][0][1]),
+                                             fmaxf(sacc[j][i][0][2], sacc[j][i][0][3])),
+                                       fmaxf(fmaxf(sacc[j][i][1][0], sacc[j][i][1][1]),
+                                             fmaxf(sacc[j][i][1][2], sacc[j][i][1][3]))));
+      lmax[i] *= c;
+      grow[i] = __builtin_amdgcn_ballot_w64(lmax[i] > m_run[i] + kRescale) != 0ull;
+      any_grow = any_grow || grow[i];
+    }
+    if (any_grow) {
+#pragma unroll
+      for (int i = 0; i < QT; ++i) {
+        if (!grow[i]) continue;
+        float tmax = fmaxf(lmax[i], partner_f32<4>(lmax[i]));  // lane l ^ 16
+        tmax = fmaxf(tmax, partner_f32<5>(tmax));              // lane l ^ 32
         const float m_new = fmaxf(m_run[i], tmax);
         const float alpha =
             (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
@@ -613,6 +636,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
         m_run[i] = m_new;
       }
+    }
+#pragma unroll
+    for (int i = 0; i < QT; ++i) {
       const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
       float psum = 0.0f;
 #pragma unroll
@@ -627,9 +653,15 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           }
       if constexpr (!kMfmaSum) l_run[i] += psum;
     }
+  };
 
-    // O^T += V^T P^T over the tile: in chunk j this lane's 8 P values are the
-    // keys wkey0 + 32 j + 8 lg .. + 7 in V^T column order, one 16-byte read
+  // V of the tile in LDS stage `stage`.  O^T += V^T P^T over the tile: in
+  // chunk j this lane's 8 P values are the keys wkey0 + 32 j + 8 lg .. + 7 in
+  // V^T column order
+  auto tile_pv = [&](int stage, const Probs& pf) {
+    const bf16_t* sv = smem + stage * Lds<D>::kStage + Lds<D>::kStageK;
+    const unsigned char* sb = smem_raw + stage * LdsDirect::kStage;
+    (void)sv; (void)sb;
 #pragma unroll
     for (int j = 0; j < PV_STEPS; ++j) {
       const int ck0 = wkey0 + 32 * j;
@@ -657,19 +689,28 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     }
   };
 
+  auto compute_tile = [&](int stage, int kt0) {
+    if (!wave_on) return;  // no live query tile in this wave (uniform)
+    Scores sacc;
+    Probs pf;
+    tile_scores(stage, sacc);
+    tile_softmax(kt0, sacc, pf);
+    tile_pv(stage, pf);
+  };
+
   // ---------------------------------------------------------------- key loop
   // LDS double buffer; PF tiles of global loads in flight.  The barrier waits
   // for this wave's LDS traffic only, so prefetched global loads stay in flight.
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
   if constexpr (DL) {
-    // NS stages: tile it lives in stage it % NS.  The loads of tile it + NS - 1
-    // go into the stage tile it - 1 used, issued after the barrier that ended
-    // its reads, so NS - 1 tiles of loads are in flight during a tile's work.
-    // Loads past the range are issued too (a zero-length range fetches
-    // nothing), which keeps the wait counts fixed.
-#pragma unroll
-    for (int t = 1; t < NS - 1; ++t) issue_tile(t, k_begin + t * kKeyTile, k_end);
-    wait_loads<(NS - 2) * DL_LOADS>();  // this wave's loads of tile 0
+    // Two LDS stages.  The scores of tile it + 1 are computed in the iteration that finishes
+    // tile it, beside its softmax and P V, so a wave has MFMA and VALU work of
+    // two tiles to interleave.  K runs one tile ahead of V in the two stages:
+    // iteration it reads K of tile it + 1 (stage (it + 1) % 2) and V of tile it
+    // (stage it % 2), and first loads K of tile it + 2 and V of tile it + 1
+    // into the stages whose K and V the previous iteration finished reading.
+    issue_rows(kbase, 1, false, k_begin + kKeyTile, k_end);
+    wait_loads<0>();  // tile 0 and K of tile 1
     if (k_begin + kKeyTile > k_end) {
       // tile 0 was loaded over every cache slot: zero its rows past the range
       // (cache slots past the sequence may hold any bits, NaN included)
@@ -682,15 +723,30 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
       }
     }
     lds_barrier();
+    Scores sacc;
+    if (wave_on) tile_scores(0, sacc);
+    lds_barrier();  // K of tile 0 is read before K of tile 2 replaces it
 #pragma unroll 1
     for (int it = 0; it < n_tiles; ++it) {
-      const int ahead = it + NS - 1;
-      issue_tile(ahead % NS, k_begin + ahead * kKeyTile, k_end);
-      compute_tile(it % NS, k_begin + it * kKeyTile);
-      wait_loads<(NS - 2) * DL_LOADS>();  // tile it + 1 has landed
+      const int cur = it & 1, nxt = cur ^ 1;
+      issue_rows(kbase, cur, false, k_begin + (it + 2) * kKeyTile, k_end);
+      issue_rows(vbase, nxt, true, k_begin + (it + 1) * kKeyTile, k_end);
+      if (wave_on) {
+        Probs pf;
+        tile_softmax(k_begin + it * kKeyTile, sacc, pf);
+        Scores snext;
+        tile_scores(nxt, snext);  // past the last tile: zeros, unused
+        tile_pv(cur, pf);
+#pragma unroll
+        for (int j = 0; j < PV_STEPS; ++j)
+#pragma unroll
+          for (int i = 0; i < QT; ++i)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) sacc[j][i][st] = snext[j][i][st];
+      }
+      wait_loads<0>();  // K of tile it + 2 and V of tile it + 1 have landed
       lds_barrier();
     }
-    wait_loads<0>();
   } else if constexpr (PF == 1) {
     store_tile(kA, vA, 0);
     lds_barrier();
@@ -977,10 +1033,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
 
 // ------------------------------------------------------------------ launchers
 
-template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, bool DL, bool ONCE>
 int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
-  auto kern = k_attn_bf16<D, NW, QT, KG, PF, NS, ONCE>;
-  const int lds = NS > 0 ? NS * LdsDirect::kStage : Lds<D>::kBytes;
+  auto kern = k_attn_bf16<D, NW, QT, KG, PF, DL, ONCE>;
+  const int lds = DL ? 2 * LdsDirect::kStage : Lds<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   hipLaunchKernelGGL(kern, dim3(p.n_slots), dim3(NW * 64), lds, s, args);
@@ -993,17 +1049,18 @@ int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
 template <int D>
 int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   const bool once = p.n_mt == 1;
-#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_, NS_)                                           \
-  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_ && p.NS == NS_)            \
-    return once ? launch_main<D, NW_, QT_, KG_, PF_, NS_, true>(p, args, s)               \
-                : launch_main<D, NW_, QT_, KG_, PF_, NS_, false>(p, args, s);
-  SPEC_ATTN_CASE(8, 1, 2, 1, 0)
-  SPEC_ATTN_CASE(8, 1, 2, 2, 0)
-  SPEC_ATTN_CASE(4, 1, 2, 2, 0)
-  SPEC_ATTN_CASE(8, 2, 1, 2, 0)
-  SPEC_ATTN_CASE(4, 2, 1, 2, 0)
-  if constexpr (D == 128) {
-    SPEC_ATTN_CASE(4, 2, 1, 2, 2)
+#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_, DL_)                                           \
+  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_ && p.DL == DL_)            \
+    return once ? launch_main<D, NW_, QT_, KG_, PF_, DL_, true>(p, args, s)               \
+                : launch_main<D, NW_, QT_, KG_, PF_, DL_, false>(p, args, s);
+  SPEC_ATTN_CASE(8, 1, 2, 1, false)
+  SPEC_ATTN_CASE(8, 1, 2, 2, false)
+  SPEC_ATTN_CASE(4, 1, 2, 2, false)
+  SPEC_ATTN_CASE(8, 2, 1, 2, false)
+  if constexpr (D == 64) {
+    SPEC_ATTN_CASE(4, 2, 1, 2, false)
+  } else {
+    SPEC_ATTN_CASE(4, 2, 1, 2, true)
   }
 #undef SPEC_ATTN_CASE
   return SPEC_ERR_UNSUPPORTED;
