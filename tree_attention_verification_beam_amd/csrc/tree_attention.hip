@@ -52,7 +52,7 @@ struct AttnPlan {
   int QT;        // 16-row query tiles per wave
   int KG;        // key groups (waves splitting one key tile)
   int PF;        // tiles of global loads in flight per workgroup (1 or 2)
-  bool DL;       // direct-to-LDS tiles, scores one tile ahead (else staged through registers)
+  int NS;        // LDS stages of direct-to-LDS tiles, scores one tile ahead (0: staged through registers)
   int n_mt;      // row blocks (workgroups sharing one key range)
   int n_splits;  // context splits
   int tiles_per_split;
@@ -98,7 +98,7 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int D, int max_ctx) {
     // stores from the waves, and the scores of the next tile run beside the
     // softmax and P V of this one
     p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 2;
-    p.DL = D == 128;
+    if (D == 128) p.NS = 2;
   }
   const long units = (long)B * Hkv;
   const int n_tiles = (max_ctx + T_cap + kKeyTile - 1) / kKeyTile;
@@ -233,10 +233,11 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
-template <int D, int NW, int QT, int KG, int PF, bool DL, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   constexpr int kThreads = NW * 64;
-  static_assert(!DL || (KG == 1 && D == 128), "direct-load plans: one key group, D = 128");
+  constexpr bool DL = NS > 0;  // direct-to-LDS tiles
+  static_assert(!DL || (KG == 1 && D == 128 && NS >= 2), "direct-load plans: one key group, D = 128");
   constexpr int RG = NW / KG;           // row groups
   constexpr int KSTEPS = D / 32;        // k-steps of Q K^T
   constexpr int DT = D / 16;            // 16-wide d tiles of the output
@@ -703,14 +704,16 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // for this wave's LDS traffic only, so prefetched global loads stay in flight.
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
   if constexpr (DL) {
-    // Two LDS stages.  The scores of tile it + 1 are computed in the iteration that finishes
-    // tile it, beside its softmax and P V, so a wave has MFMA and VALU work of
-    // two tiles to interleave.  K runs one tile ahead of V in the two stages:
-    // iteration it reads K of tile it + 1 (stage (it + 1) % 2) and V of tile it
-    // (stage it % 2), and first loads K of tile it + 2 and V of tile it + 1
-    // into the stages whose K and V the previous iteration finished reading.
-    issue_rows(kbase, 1, false, k_begin + kKeyTile, k_end);
-    wait_loads<0>();  // tile 0 and K of tile 1
+    // NS LDS stages, K one tile ahead of V.  The scores of tile it + 1 are
+    // computed in the iteration that finishes tile it, beside its softmax and
+    // P V, so a wave has MFMA and VALU work of two tiles to interleave.
+    // Iteration it reads K of tile it + 1 (stage (it + 1) % NS) and V of tile
+    // it (stage it % NS), and first loads K of tile it + NS and V of tile
+    // it + NS - 1 into the stages whose K and V the previous iteration
+    // finished reading; NS - 1 iterations pass before they are needed.
+    for (int t = 1; t < NS; ++t) issue_rows(kbase, t % NS, false, k_begin + t * kKeyTile, k_end);
+    for (int t = 1; t < NS - 1; ++t) issue_rows(vbase, t % NS, true, k_begin + t * kKeyTile, k_end);
+    wait_loads<0>();
     if (k_begin + kKeyTile > k_end) {
       // tile 0 was loaded over every cache slot: zero its rows past the range
       // (cache slots past the sequence may hold any bits, NaN included)
@@ -725,12 +728,14 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     lds_barrier();
     Scores sacc;
     if (wave_on) tile_scores(0, sacc);
-    lds_barrier();  // K of tile 0 is read before K of tile 2 replaces it
+    lds_barrier();  // K of tile 0 is read before K of tile NS replaces it
+    int cur = 0;  // it % NS
 #pragma unroll 1
     for (int it = 0; it < n_tiles; ++it) {
-      const int cur = it & 1, nxt = cur ^ 1;
-      issue_rows(kbase, cur, false, k_begin + (it + 2) * kKeyTile, k_end);
-      issue_rows(vbase, nxt, true, k_begin + (it + 1) * kKeyTile, k_end);
+      const int nxt = cur + 1 == NS ? 0 : cur + 1;
+      const int prv = cur == 0 ? NS - 1 : cur - 1;
+      issue_rows(kbase, cur, false, k_begin + (it + NS) * kKeyTile, k_end);
+      issue_rows(vbase, prv, true, k_begin + (it + NS - 1) * kKeyTile, k_end);
       if (wave_on) {
         Probs pf;
         tile_softmax(k_begin + it * kKeyTile, sacc, pf);
@@ -744,9 +749,13 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
             for (int st = 0; st < 2; ++st) sacc[j][i][st] = snext[j][i][st];
       }
-      wait_loads<0>();  // K of tile it + 2 and V of tile it + 1 have landed
+      // K of tile it + 2 and V of tile it + 1 have landed (the loads of the
+      // last NS - 2 iterations may still be in flight)
+      wait_loads<(NS - 2) * 2 * DL_BLOCKS>();
       lds_barrier();
+      cur = nxt;
     }
+    wait_loads<0>();
   } else if constexpr (PF == 1) {
     store_tile(kA, vA, 0);
     lds_barrier();
@@ -1033,10 +1042,10 @@ __global__ __launch_bounds__(256) void k_attn_f32(int B, int T_cap, int H, int H
 
 // ------------------------------------------------------------------ launchers
 
-template <int D, int NW, int QT, int KG, int PF, bool DL, bool ONCE>
+template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
 int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
-  auto kern = k_attn_bf16<D, NW, QT, KG, PF, DL, ONCE>;
-  const int lds = DL ? 2 * LdsDirect::kStage : Lds<D>::kBytes;
+  auto kern = k_attn_bf16<D, NW, QT, KG, PF, NS, ONCE>;
+  const int lds = NS > 0 ? NS * LdsDirect::kStage : Lds<D>::kBytes;
   (void)hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   hipLaunchKernelGGL(kern, dim3(p.n_slots), dim3(NW * 64), lds, s, args);
@@ -1049,18 +1058,18 @@ int launch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
 template <int D>
 int dispatch_main(const AttnPlan& p, const AttnArgs& args, hipStream_t s) {
   const bool once = p.n_mt == 1;
-#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_, DL_)                                           \
-  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_ && p.DL == DL_)            \
-    return once ? launch_main<D, NW_, QT_, KG_, PF_, DL_, true>(p, args, s)               \
-                : launch_main<D, NW_, QT_, KG_, PF_, DL_, false>(p, args, s);
-  SPEC_ATTN_CASE(8, 1, 2, 1, false)
-  SPEC_ATTN_CASE(8, 1, 2, 2, false)
-  SPEC_ATTN_CASE(4, 1, 2, 2, false)
-  SPEC_ATTN_CASE(8, 2, 1, 2, false)
+#define SPEC_ATTN_CASE(NW_, QT_, KG_, PF_, NS_)                                           \
+  if (p.NW == NW_ && p.QT == QT_ && p.KG == KG_ && p.PF == PF_ && p.NS == NS_)            \
+    return once ? launch_main<D, NW_, QT_, KG_, PF_, NS_, true>(p, args, s)               \
+                : launch_main<D, NW_, QT_, KG_, PF_, NS_, false>(p, args, s);
+  SPEC_ATTN_CASE(8, 1, 2, 1, 0)
+  SPEC_ATTN_CASE(8, 1, 2, 2, 0)
+  SPEC_ATTN_CASE(4, 1, 2, 2, 0)
+  SPEC_ATTN_CASE(8, 2, 1, 2, 0)
   if constexpr (D == 64) {
-    SPEC_ATTN_CASE(4, 2, 1, 2, false)
+    SPEC_ATTN_CASE(4, 2, 1, 2, 0)
   } else {
-    SPEC_ATTN_CASE(4, 2, 1, 2, true)
+    SPEC_ATTN_CASE(4, 2, 1, 2, 2)
   }
 #undef SPEC_ATTN_CASE
   return SPEC_ERR_UNSUPPORTED;
