@@ -95,6 +95,15 @@ __device__ inline float wave_max_f32(float v) {
   return fmaxf(v, partner_f32<5>(v));
 }
 
+__device__ inline int wave_min_i32(int v) {
+  v = min(v, partner_i32<0>(v));
+  v = min(v, partner_i32<1>(v));
+  v = min(v, partner_i32<2>(v));
+  v = min(v, partner_i32<3>(v));
+  v = min(v, partner_i32<4>(v));
+  return min(v, partner_i32<5>(v));
+}
+
 __device__ inline double wave_sum_f64(double v) {
   v += partner_f64<0>(v);
   v += partner_f64<1>(v);

@@ -237,39 +237,54 @@ __global__ __launch_bounds__(kStatThreads) void k_vstats(
       for (int i = 0; i < 4; ++i) x[4 * j + i] = e + i < V ? row[e + i] : -INFINITY;
     }
   }
-  // local max / argmax in increasing index order
-  // (a stays INT_MAX until the first valid element, which is always taken)
-  float m = -INFINITY;
-  int a = 0x7fffffff;
+  // Row maximum, then (in one more pass over the registers) the sum of
+  // exp(l - m) and the lowest index holding the maximum.  Padding past V is
+  // -inf: it never raises the maximum and, having the highest indices, never
+  // wins a tie, so only the sum needs the range test, and only in the last
+  // chunk of a row.
+  float tm = x[0];  // this thread's maximum
 #pragma unroll
-  for (int j = 0; j < EPT / 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (idx0[j] + i < V && (a == 0x7fffffff || x[4 * j + i] > m)) {
-        m = x[4 * j + i];
-        a = idx0[j] + i;
-      }
-  wave_argmax(m, a);
+  for (int e = 1; e < EPT; ++e) tm = fmaxf(tm, x[e]);
+  float m = wave_max_f32(tm);
   const int wave = tid >> 6, lane = tid & 63;
+  if (lane == 0) s_m[wave] = m;
+  __syncthreads();
+  m = s_m[0];
+  for (int w = 1; w < kStatThreads / 64; ++w) m = fmaxf(m, s_m[w]);
+  // sum of exp(l - m): exp in fp32 (v_exp_f32 on the log2 argument), sums in
+  // fp64; both passes run in increasing index order
+  float loc = 0.0f;
+  const float mb = m * kLog2e;
+  const bool full = base + EPT * kStatThreads <= V;  // uniform
+  if (full) {
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) loc += __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], kLog2e, -mb));
+  } else {
+#pragma unroll
+    for (int j = 0; j < EPT / 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (idx0[j] + i < V) loc += __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * j + i], kLog2e, -mb));
+  }
+  // the lowest index holding the maximum: only lanes whose own maximum is it
+  // search (usually one lane of one wave)
+  int a = 0x7fffffff;
+  if (tm == m) {
+#pragma unroll
+    for (int j = EPT / 4 - 1; j >= 0; --j)
+#pragma unroll
+      for (int i = 3; i >= 0; --i) a = x[4 * j + i] == m ? idx0[j] + i : a;
+  }
+  a = wave_min_i32(a);
+  double s = wave_sum_f64((double)loc);
   if (lane == 0) {
-    s_m[wave] = m;
+    s_s[wave] = s;
     s_a[wave] = a;
   }
   __syncthreads();
-  m = s_m[0];
   a = s_a[0];
-  for (int w = 1; w < kStatThreads / 64; ++w) argmax_merge(m, a, s_m[w], s_a[w]);
-  // sum of exp(l - m): exp in fp32 (v_exp_f32 on the log2 argument), sums in fp64
-  float loc = 0.0f;
-  const float mb = m * kLog2e;
-#pragma unroll
-  for (int j = 0; j < EPT / 4; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (idx0[j] + i < V) loc += __builtin_amdgcn_exp2f(__builtin_fmaf(x[4 * j + i], kLog2e, -mb));
-  double s = wave_sum_f64((double)loc);
-  if (lane == 0) s_s[wave] = s;
-  __syncthreads();
+  for (int w = 1; w < kStatThreads / 64; ++w) a = min(a, s_a[w]);
+  if (a == 0x7fffffff) a = base;  // no element equals the maximum (NaN logits): stay in range
   if (tid == 0) {
     double tot = 0.0;
     for (int w = 0; w < kStatThreads / 64; ++w) tot += s_s[w];
