@@ -8,7 +8,8 @@
 - a context that overflows the launch bound: that sequence gets zero rows and
   the device status bit, the others stay exact;
 - B = 0 calls (host-only, in test_abi.py);
-- one attention call launched forty times, each checked (intermittent errors);
+- one attention call launched forty times, each checked (intermittent errors),
+  on the staged plan and on the direct-to-LDS GQA plan;
 - the greedy walk on explicit trees whose siblings share tokens (several
   survivors per depth), on a vocabulary that is not a multiple of 4 (scalar
   loads) and on a tree that fails validation.
@@ -143,6 +144,28 @@ def test_attention_repeated_launches_match(gpu):
     so one launch is not enough."""
     inp = synth.make_inputs(4, 100, B_override=1, ctx_override=3000)
     log("case repeated attention launches, B=1 ctx=3000 G=4")
+    tr = oracle_tree(inp)
+    ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
+                                tr["anc"])
+    step = pipeline.Step(inp, "greedy")
+    step.build_tree()
+    for rep in range(40):
+        step.out.fill_(float("nan"))
+        step.attention()
+        torch.cuda.synchronize()
+        assert int(step.status.item()) == 0
+        attn_bar(step.out.float().cpu().numpy(), ref, f"launch {rep}")
+
+
+def test_direct_load_attention_repeated_launches_match(gpu):
+    """Forty launches of the 70B-class GQA plan that loads its K/V tiles
+    straight into LDS and computes the next tile's scores beside this tile's
+    softmax (two sequences, 1000-key contexts: five 128-row blocks per key
+    range, six context splits, the tree keys in the last split).  Every
+    launch must match the oracle, so that a race between the loads into LDS
+    and the barrier that hands a stage over would show."""
+    inp = synth.make_inputs(3, 100, B_override=2, ctx_override=1000)
+    log("case repeated direct-load attention launches, B=2 ctx=1000 G=8")
     tr = oracle_tree(inp)
     ref = oracle.tree_attention(inp["q"], inp["k"], inp["v"], inp["ctx_len"], tr["n_nodes"],
                                 tr["anc"])
