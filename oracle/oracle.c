@@ -33,13 +33,12 @@
  *   - Padding: parent/token/depth = -1 and an all-zero mask for t >= T.
  *
  * Pins: every function is checked in the test suite against values the pages
- * print, closed forms, brute force or a second formulation, with one
- * exception.  PARITY UNPINNED: the tree-level output distribution of per-path
- * rejection (mode 1) when a node has two or more children.  That mode is not
- * distribution-exact then (only sequential checking is), so no target
- * distribution exists to test it against; only its agreement with an
- * independent per-beam formulation, and its single-child case (plain
- * speculative sampling, chi-square), are pinned.
+ * print, closed forms, brute force or a second formulation.  Per-path
+ * rejection (mode 1) is not distribution-exact when a node has two or more
+ * children (only sequential checking is), so its tree-level output law is
+ * pinned to its own definition instead: the joint law of (stop node, next
+ * token) on a fixed tree with siblings, summed exactly over every accept
+ * pattern, against 1e6 seeded trials.
  */
 #include <math.h>
 #include <stdint.h>

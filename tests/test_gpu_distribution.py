@@ -19,6 +19,11 @@ numbers.  Per case:
 - on the first call of each case every tree output, decision, path and drawn
   token equals the oracle's, sequences with a near-tie on either side excepted
   (they are counted and must stay rare).
+Per-path rejection on a fixed tree with siblings at two depths (V = 6), in the
+one-pass and the walk formulation: the joint law of (stop node, next token)
+over 1e6 trials passes a chi-square test against the exact table summed over
+every accept pattern (tests/exact_paths.py), with the oracle's inputs and
+element-wise parity on the first call.
 Two positions (V = 8): a root with 3 i.i.d. children, each with 2 i.i.d.
 children of its own, and rows that depend only on the token prefix.  The first
 emitted token follows p0 and, given first token x, the second follows p1[x]
@@ -35,6 +40,7 @@ from scipy.special import softmax
 
 import oracle
 from tree_attention_verification_beam_amd import pipeline, synth
+from test_oracle_verify import fixed_tree_counts, fixed_tree_tables, table_pvalue
 
 pytestmark = pytest.mark.gpu
 
@@ -153,6 +159,43 @@ def test_per_path_rejection_siblings_is_not_exact(gpu):
     pv = _chi2_pvalue(counts, softmax(lp.astype(np.float64)))
     log(f"  chi-square p-value {pv:.3g}")
     assert pv < 1e-3
+
+
+@pytest.mark.parametrize("mode", ["reject_path", "reject_path_walk"])
+def test_per_path_rejection_tree_matches_exact_enumeration(gpu, mode):
+    log(f"case per-path rejection ({mode}) on a fixed 8-node tree, {TRIALS} trials at V=6")
+    first = [True]
+
+    def run(inp):
+        res = pipeline.Step(inp, mode=mode, device="cuda:0", with_kv=False).run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        if first[0]:
+            first[0] = False
+            tr = oracle.build_tree_explicit(inp["cand_parent"], inp["cand_token"],
+                                            inp["root_token"], inp["T_cap"])
+            for k in ("n_nodes", "parent", "token", "depth"):
+                assert np.array_equal(res[k], tr[k]), k
+            args = (inp["tgt"], inp["dft"], inp["dft_row"], tr["n_nodes"], tr["parent"],
+                    tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
+            ora = (oracle.verify("reject_path", *args) if mode == "reject_path"
+                   else oracle.verify_reject_walk("reject_path", *args))
+            ok = (res["near_tie"] == 0) & (ora["near_tie"] == 0)
+            n_tie = int((~ok).sum())
+            log(f"  {n_tie} of {len(ok)} sequences with a near-tie")
+            assert n_tie <= len(ok) // 1000
+            for k in ("acc_len", "acc_path", "next_token", "decision"):
+                assert np.array_equal(res[k][ok], ora[k][ok]), k
+        return res
+
+    counts = fixed_tree_counts(run, TRIALS, seed=1912)
+    tables = fixed_tree_tables()
+    pv = table_pvalue(counts, tables["exact"])
+    log(f"  chi-square p-value against the exact table {pv:.4f}; stop nodes "
+        f"{np.round(counts.sum(axis=1) / TRIALS, 3).tolist()}")
+    assert pv >= 1e-3
+    for v, tab in tables.items():
+        if v != "exact":
+            assert table_pvalue(counts, tab) < 1e-3, v
 
 
 # ----------------------------------------------------------------------------

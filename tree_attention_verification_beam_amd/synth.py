@@ -314,3 +314,56 @@ def make_two_level_trials(rng: np.random.Generator, B: int, lp0: np.ndarray, lq0
                 cand_token=cand_token, root_token=np.zeros(B, np.int32), tgt=tgt, dft=dft,
                 dft_row=dft_row, u_node=exact_uniforms(rng, (B, T_cap)),
                 u_final=exact_uniforms(rng, (B,)))
+
+
+# one fixed small tree with siblings at several depths: parent node of candidate
+# nodes 1..7 and their tokens (vocabulary of 6); nodes 0, 1, 2 and 4 have children
+FIXED_TREE_PARENTS = (0, 0, 0, 1, 1, 2, 4)
+FIXED_TREE_TOKENS = (0, 1, 2, 3, 4, 0, 5)
+
+
+def make_fixed_tree_trials(rng: np.random.Generator, B: int, cand_parent, cand_token,
+                           lp: np.ndarray, lq: np.ndarray, dft_row) -> dict:
+    """B independent trials of one fixed explicit tree; only the uniforms differ.
+
+    `cand_parent` / `cand_token` name candidate nodes 1..N (parents are node
+    indices, the root is node 0), `lp` holds the target logits row of every node
+    (T = N + 1 rows), `lq` the draft logits rows and `dft_row[t]` the draft row
+    of node t's children (-1 for a leaf).
+    """
+    cand_parent = np.asarray(cand_parent, np.int32)
+    cand_token = np.asarray(cand_token, np.int32)
+    lp = np.asarray(lp, np.float32)
+    lq = np.asarray(lq, np.float32)
+    N = len(cand_parent)
+    T_cap = N + 1
+    V = lp.shape[1]
+    return dict(B=B, T_cap=T_cap, V=V, tree="explicit",
+                cand_parent=np.ascontiguousarray(np.broadcast_to(cand_parent, (B, N))),
+                cand_token=np.ascontiguousarray(np.broadcast_to(cand_token, (B, N))),
+                root_token=np.zeros(B, np.int32),
+                tgt=np.ascontiguousarray(np.broadcast_to(lp, (B, T_cap, V))),
+                dft=np.ascontiguousarray(np.broadcast_to(lq, (B,) + lq.shape)),
+                dft_row=np.ascontiguousarray(np.broadcast_to(np.asarray(dft_row, np.int32),
+                                                             (B, T_cap))),
+                u_node=exact_uniforms(rng, (B, T_cap)), u_final=exact_uniforms(rng, (B,)))
+
+
+FIXED_TREE_DFT_ROW = (0, 1, 2, -1, 3, -1, -1, -1)
+
+
+def fixed_tree_logits(seed: int) -> tuple:
+    """Logits rows of the fixed tree: target row of every node ~ N(0, 1.5^2),
+    draft row of each node with children = its target row + N(0, 1), with each
+    child's token raised by 0.5 in its parent's draft row (drafted tokens are
+    the draft's likely ones).  Returns (lp (8, 6), lq (4, 6), dft_row)."""
+    rng = np.random.default_rng(seed)
+    T = len(FIXED_TREE_PARENTS) + 1
+    lp = (1.5 * rng.standard_normal((T, 6))).astype(np.float32)
+    lq = np.empty((4, 6), np.float32)
+    for node, r in enumerate(FIXED_TREE_DFT_ROW):
+        if r >= 0:
+            lq[r] = lp[node] + rng.standard_normal(6).astype(np.float32)
+    for par, tok in zip(FIXED_TREE_PARENTS, FIXED_TREE_TOKENS):
+        lq[FIXED_TREE_DFT_ROW[par], tok] += np.float32(0.5)
+    return lp, lq, np.asarray(FIXED_TREE_DFT_ROW, np.int32)
