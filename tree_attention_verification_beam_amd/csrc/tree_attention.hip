@@ -26,7 +26,9 @@
 // (no GQA, small trees) the waves split each key tile instead (KG key groups)
 // and combine through LDS at the end.  The running maximum is only moved when
 // a score exceeds it by more than 2^8, so most tiles skip the rescale of the
-// accumulators; the result is the same softmax.  Context keys are unmasked;
+// accumulators; the result is the same softmax (on the direct-load plan the
+// exponentials are taken first and the test is an integer maximum of their
+// bits, exceeding 2^8).  Context keys are unmasked;
 // only tiles that reach the tree slots test the ancestor bits.  Long contexts
 // are split across workgroups (chosen so the grid fills the 256 CUs evenly) and
 // a merge kernel combines the (max, sum, O) partials.
@@ -52,7 +54,7 @@ struct AttnPlan {
   int QT;        // 16-row query tiles per wave
   int KG;        // key groups (waves splitting one key tile)
   int PF;        // tiles of global loads in flight per workgroup (1 or 2)
-  int NS;        // LDS stages of direct-to-LDS tiles, scores one tile ahead (0: staged through registers)
+  int NS;        // LDS stages of direct-to-LDS tiles, scores one tile ahead (2; 0: staged through registers)
   int n_mt;      // row blocks (workgroups sharing one key range)
   int n_splits;  // context splits
   int tiles_per_split;
@@ -233,11 +235,16 @@ __device__ inline void slot_to_work(int slot, int n_mt, int& kv_unit, int& mt) {
   mt = j - (j / n_mt) * n_mt;
 }
 
+template <int S>
+struct StageC {
+  static constexpr int value = S;
+};
+
 template <int D, int NW, int QT, int KG, int PF, int NS, bool ONCE>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs a) {
   constexpr int kThreads = NW * 64;
   constexpr bool DL = NS > 0;  // direct-to-LDS tiles
-  static_assert(!DL || (KG == 1 && D == 128 && NS >= 2), "direct-load plans: one key group, D = 128");
+  static_assert(!DL || (KG == 1 && D == 128 && NS == 2), "direct-load plans: one key group, D = 128, two stages");
   constexpr int RG = NW / KG;           // row groups
   constexpr int KSTEPS = D / 32;        // k-steps of Q K^T
   constexpr int DT = D / 16;            // 16-wide d tiles of the output
@@ -600,59 +607,136 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
             }
     }
 
-    // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
-    // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e.  A row maximum moves only when some
-    // lane outgrew it by 2^kRescale; then the 4 lane groups holding the row
-    // agree on the new maximum.  One uniform branch covers every query tile's
-    // rescale, so the exponentials of all tiles share one basic block with
-    // whatever MFMA work follows.
-    float lmax[QT];
-    bool grow[QT];
-    bool any_grow = false;
-#pragma unroll
-    for (int i = 0; i < QT; ++i) {
-      lmax[i] = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < PV_STEPS; ++j)
-        lmax[i] = fmaxf(lmax[i], fmaxf(fmaxf(fmaxf(sacc[j][i][0][0], sacc[j][i][0][1]),
-                                             fmaxf(sacc[j][i][0][2], sacc[j][i][0][3])),
-                                       fmaxf(fmaxf(sacc[j][i][1][0], sacc[j][i][1][1]),
-                                             fmaxf(sacc[j][i][1][2], sacc[j][i][1][3]))));
-      lmax[i] *= c;
-      grow[i] = __builtin_amdgcn_ballot_w64(lmax[i] > m_run[i] + kRescale) != 0ull;
-      any_grow = any_grow || grow[i];
-    }
-    if (any_grow) {
+    if constexpr (DL) {
+      // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
+      // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e.  The exponentials are taken
+      // against the running maximum first, and the maximum moves only when one
+      // of them exceeds 2^kRescale (or on a row's first tile): an integer
+      // maximum over the bit patterns of these non-negative values orders them
+      // as floats and, unlike a float maximum of the MFMA results, needs no
+      // quieting of each operand.  A growing query tile then takes its row
+      // maximum (the 4 lane groups holding the row agree on it), rescales its
+      // accumulators and takes its exponentials again; one uniform branch
+      // covers every query tile's rescale.
+      static_assert(kRescale == 8.0f, "growth threshold bits below");
+      constexpr uint32_t kGrowBits = 0x43800000u;  // 2^kRescale as fp32 bits
+      bool grow[QT];
+      bool any_grow = false;
+      float psum[QT];
 #pragma unroll
       for (int i = 0; i < QT; ++i) {
-        if (!grow[i]) continue;
-        float tmax = fmaxf(lmax[i], partner_f32<4>(lmax[i]));  // lane l ^ 16
-        tmax = fmaxf(tmax, partner_f32<5>(tmax));              // lane l ^ 32
-        const float m_new = fmaxf(m_run[i], tmax);
-        const float alpha =
-            (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
-        l_run[i] *= alpha;
-        acc_l[i] *= alpha;
+        const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
+        uint32_t pmax = 0u;
+        psum[i] = 0.0f;
 #pragma unroll
-        for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
-        m_run[i] = m_new;
+        for (int j = 0; j < PV_STEPS; ++j)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
+              pf[j][i][4 * st + e] = (bf16_t)pv;
+              pmax = max(pmax, __builtin_bit_cast(uint32_t, pv));
+              if constexpr (!kMfmaSum) psum[i] += pv;
+            }
+        grow[i] = __builtin_amdgcn_ballot_w64(pmax > kGrowBits || m_run[i] == -INFINITY) != 0ull;
+        any_grow = any_grow || grow[i];
       }
-    }
+      if (any_grow) {
 #pragma unroll
-    for (int i = 0; i < QT; ++i) {
-      const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
-      float psum = 0.0f;
+        for (int i = 0; i < QT; ++i) {
+          if (!grow[i]) continue;
+          float lmax = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < PV_STEPS; ++j)
+          for (int j = 0; j < PV_STEPS; ++j)
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
-            pf[j][i][4 * st + e] = (bf16_t)pv;
-            if constexpr (!kMfmaSum) psum += pv;
-          }
-      if constexpr (!kMfmaSum) l_run[i] += psum;
+              for (int e = 0; e < 4; ++e) lmax = fmaxf(lmax, sacc[j][i][st][e]);
+          lmax *= c;
+          float tmax = fmaxf(lmax, partner_f32<4>(lmax));  // lane l ^ 16
+          tmax = fmaxf(tmax, partner_f32<5>(tmax));        // lane l ^ 32
+          const float m_new = fmaxf(m_run[i], tmax);
+          const float alpha =
+              (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+          l_run[i] *= alpha;
+          acc_l[i] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
+          m_run[i] = m_new;
+          const float nmu = m_new == -INFINITY ? 0.0f : -m_new;
+          psum[i] = 0.0f;
+#pragma unroll
+          for (int j = 0; j < PV_STEPS; ++j)
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
+                pf[j][i][4 * st + e] = (bf16_t)pv;
+                if constexpr (!kMfmaSum) psum[i] += pv;
+              }
+        }
+      }
+      if constexpr (!kMfmaSum) {
+#pragma unroll
+        for (int i = 0; i < QT; ++i) l_run[i] += psum[i];
+      }
+    } else {
+      // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
+      // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e.  A row maximum moves only when some
+      // lane outgrew it by 2^kRescale; then the 4 lane groups holding the row
+      // agree on the new maximum.  One uniform branch covers every query tile's
+      // rescale, so the exponentials of all tiles share one basic block with
+      // whatever MFMA work follows.
+      float lmax[QT];
+      bool grow[QT];
+      bool any_grow = false;
+#pragma unroll
+      for (int i = 0; i < QT; ++i) {
+        lmax[i] = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < PV_STEPS; ++j)
+          lmax[i] = fmaxf(lmax[i], fmaxf(fmaxf(fmaxf(sacc[j][i][0][0], sacc[j][i][0][1]),
+                                               fmaxf(sacc[j][i][0][2], sacc[j][i][0][3])),
+                                         fmaxf(fmaxf(sacc[j][i][1][0], sacc[j][i][1][1]),
+                                               fmaxf(sacc[j][i][1][2], sacc[j][i][1][3]))));
+        lmax[i] *= c;
+        grow[i] = __builtin_amdgcn_ballot_w64(lmax[i] > m_run[i] + kRescale) != 0ull;
+        any_grow = any_grow || grow[i];
+      }
+      if (any_grow) {
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+          if (!grow[i]) continue;
+          float tmax = fmaxf(lmax[i], partner_f32<4>(lmax[i]));  // lane l ^ 16
+          tmax = fmaxf(tmax, partner_f32<5>(tmax));              // lane l ^ 32
+          const float m_new = fmaxf(m_run[i], tmax);
+          const float alpha =
+              (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
+          l_run[i] *= alpha;
+          acc_l[i] *= alpha;
+#pragma unroll
+          for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
+          m_run[i] = m_new;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < QT; ++i) {
+        const float nmu = m_run[i] == -INFINITY ? 0.0f : -m_run[i];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PV_STEPS; ++j)
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
+              pf[j][i][4 * st + e] = (bf16_t)pv;
+              if constexpr (!kMfmaSum) psum += pv;
+            }
+        if constexpr (!kMfmaSum) l_run[i] += psum;
+      }
     }
   };
 
@@ -704,13 +788,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   // for this wave's LDS traffic only, so prefetched global loads stay in flight.
   const int n_tiles = (k_end - k_begin + kKeyTile - 1) / kKeyTile;
   if constexpr (DL) {
-    // NS LDS stages, K one tile ahead of V.  The scores of tile it + 1 are
+    // Two LDS stages, K one tile ahead of V.  The scores of tile it + 1 are
     // computed in the iteration that finishes tile it, beside its softmax and
     // P V, so a wave has MFMA and VALU work of two tiles to interleave.
-    // Iteration it reads K of tile it + 1 (stage (it + 1) % NS) and V of tile
-    // it (stage it % NS), and first loads K of tile it + NS and V of tile
-    // it + NS - 1 into the stages whose K and V the previous iteration
-    // finished reading; NS - 1 iterations pass before they are needed.
+    // Iteration it reads K of tile it + 1 (stage (it + 1) & 1) and V of tile
+    // it (stage it & 1), and first loads K of tile it + 2 and V of tile it + 1
+    // into the stages whose K and V the previous iteration finished reading.
     for (int t = 1; t < NS; ++t) issue_rows(kbase, t % NS, false, k_begin + t * kKeyTile, k_end);
     for (int t = 1; t < NS - 1; ++t) issue_rows(vbase, t % NS, true, k_begin + t * kKeyTile, k_end);
     wait_loads<0>();
@@ -729,13 +812,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     Scores sacc;
     if (wave_on) tile_scores(0, sacc);
     lds_barrier();  // K of tile 0 is read before K of tile NS replaces it
-    int cur = 0;  // it % NS
-#pragma unroll 1
-    for (int it = 0; it < n_tiles; ++it) {
-      const int nxt = cur + 1 == NS ? 0 : cur + 1;
-      const int prv = cur == 0 ? NS - 1 : cur - 1;
+    // one iteration per tile, unrolled by the two stages so that every LDS
+    // address is a constant offset from a per-lane base
+    auto dl_iter = [&](auto cur_c, int it) {
+      constexpr int cur = decltype(cur_c)::value, nxt = 1 - cur;
       issue_rows(kbase, cur, false, k_begin + (it + NS) * kKeyTile, k_end);
-      issue_rows(vbase, prv, true, k_begin + (it + NS - 1) * kKeyTile, k_end);
+      issue_rows(vbase, nxt, true, k_begin + (it + NS - 1) * kKeyTile, k_end);
       if (wave_on) {
         Probs pf;
         tile_softmax(k_begin + it * kKeyTile, sacc, pf);
@@ -749,12 +831,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 #pragma unroll
             for (int st = 0; st < 2; ++st) sacc[j][i][st] = snext[j][i][st];
       }
-      // K of tile it + 2 and V of tile it + 1 have landed (the loads of the
-      // last NS - 2 iterations may still be in flight)
-      wait_loads<(NS - 2) * 2 * DL_BLOCKS>();
+      // K of tile it + 2 and V of tile it + 1 have landed
+      wait_loads<0>();
       lds_barrier();
-      cur = nxt;
+    };
+    int it = 0;
+#pragma unroll 1
+    for (; it + 2 <= n_tiles; it += 2) {
+      dl_iter(StageC<0>{}, it);
+      dl_iter(StageC<1>{}, it + 1);
     }
+    if (it < n_tiles) dl_iter(StageC<0>{}, it);
     wait_loads<0>();
   } else if constexpr (PF == 1) {
     store_tile(kA, vA, 0);
