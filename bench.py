@@ -57,9 +57,15 @@ def parse():
     return ap.parse_args()
 
 
+ATTENTION_SOURCES = ("tree_attention.hip", "attn_bf16.hpp", "attn_direct.hip", "tile_mask.hpp")
+
+
 def kernel_source_hash() -> str:
-    src = ROOT / "tree_attention_verification_beam_amd" / "csrc" / "tree_attention.hip"
-    return hashlib.sha256(src.read_bytes()).hexdigest()
+    """sha256 over the attention's sources, in a fixed order."""
+    h = hashlib.sha256()
+    for name in ATTENTION_SOURCES:
+        h.update((ROOT / "tree_attention_verification_beam_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()
 
 
 def counted_traffic(workload: str):

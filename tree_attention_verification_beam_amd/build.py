@@ -2,7 +2,8 @@
 
 Every ``csrc/*.hip`` file is compiled to an object (in parallel) and linked
 into ``libspecverify.so`` next to this file.  Flags: -O3, C++17, gfx950 only,
-packed fp32 arithmetic disabled.
+packed fp32 arithmetic disabled; the direct-to-LDS attention plan's unit also
+takes the backend's max-ilp scheduling strategy.
 """
 from __future__ import annotations
 
@@ -21,11 +22,16 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-result"]
+# Flags of single sources.  The direct-to-LDS attention plan is scheduled with
+# the backend's max-ilp strategy (70B-class GQA attention 246.9 -> 238.0 us in
+# interleaved A/B); the register-staged plans ran slower under it (multi-
+# candidate attention 144 -> 160 us), so they keep the default.
+EXTRA = {"attn_direct.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _compile(src: Path) -> Path:
     obj = BUILD / (src.stem + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", str(src), "-o", str(obj)]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src.name, []), "-c", str(src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in res.stderr.splitlines() if "not a recognized feature" not in l)
     if res.returncode != 0:
