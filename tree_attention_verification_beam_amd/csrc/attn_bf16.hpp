@@ -3,6 +3,12 @@
 // register-staged plans in tree_attention.hip (which states the method and
 // chooses the plan) and the direct-to-LDS plan in attn_direct.hip, which the
 // build compiles with a scheduling strategy of its own.
+//
+// The kernel computes the one forward pass over the packed tree of
+// "Recurrent Drafter for Fast Speculative Decoding in Large Language Models",
+// section "The Full Speculative Decoding Loop", Step 4, under the ancestor
+// mask of "Clover: Regressive Lightweight Speculative Decoding with
+// Sequential Knowledge" (causal mask construction).
 #pragma once
 #include "common.hpp"
 #include "tile_mask.hpp"
