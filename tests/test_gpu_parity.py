@@ -108,7 +108,7 @@ def attn_bar(gpu_rows, ref_rows, what):
 # --------------------------------------------------------------------------- reduced cases
 
 @pytest.mark.parametrize("wid", [0, 1, 2, 3, 4])
-@pytest.mark.parametrize("seed", [100, 200])
+@pytest.mark.parametrize("seed", [100, 200, 300])
 def test_reduced_workload(gpu, wid, seed):
     inp = synth.make_inputs(wid, seed, **REDUCED[wid])
     log(f"case reduced wid={wid} seed={seed} B={inp['B']} ctx={inp['ctx']}")
