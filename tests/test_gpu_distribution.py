@@ -19,8 +19,8 @@ numbers.  Per case:
 - on the first call of each case every tree output, decision, path and drawn
   token equals the oracle's, sequences with a near-tie on either side excepted
   (they are counted and must stay rare).
-Per-path rejection on a fixed tree with siblings at two depths (V = 6), in the
-one-pass and the walk formulation: the joint law of (stop node, next token)
+Per-path rejection on a fixed tree with siblings at two depths (V = 6; also with
+two children of the root sharing a token), in the one-pass and the walk formulation: the joint law of (stop node, next token)
 over 1e6 trials passes a chi-square test against the exact table summed over
 every accept pattern (tests/exact_paths.py), with the oracle's inputs and
 element-wise parity on the first call.
@@ -40,7 +40,7 @@ from scipy.special import softmax
 
 import oracle
 from tree_attention_verification_beam_amd import pipeline, synth
-from test_oracle_verify import fixed_tree_counts, fixed_tree_tables, table_pvalue
+from test_oracle_verify import FIXED_CASES, fixed_tree_counts, fixed_tree_tables, table_pvalue
 
 pytestmark = pytest.mark.gpu
 
@@ -161,9 +161,10 @@ def test_per_path_rejection_siblings_is_not_exact(gpu):
     assert pv < 1e-3
 
 
+@pytest.mark.parametrize("case", list(FIXED_CASES))
 @pytest.mark.parametrize("mode", ["reject_path", "reject_path_walk"])
-def test_per_path_rejection_tree_matches_exact_enumeration(gpu, mode):
-    log(f"case per-path rejection ({mode}) on a fixed 8-node tree, {TRIALS} trials at V=6")
+def test_per_path_rejection_tree_matches_exact_enumeration(gpu, mode, case):
+    log(f"case per-path rejection ({mode}) on a fixed 8-node tree ({case}), {TRIALS} trials at V=6")
     first = [True]
 
     def run(inp):
@@ -187,8 +188,8 @@ def test_per_path_rejection_tree_matches_exact_enumeration(gpu, mode):
                 assert np.array_equal(res[k][ok], ora[k][ok]), k
         return res
 
-    counts = fixed_tree_counts(run, TRIALS, seed=1912)
-    tables = fixed_tree_tables()
+    counts = fixed_tree_counts(run, TRIALS, seed=1912, case=case)
+    tables = fixed_tree_tables(case)
     pv = table_pvalue(counts, tables["exact"])
     log(f"  chi-square p-value against the exact table {pv:.4f}; stop nodes "
         f"{np.round(counts.sum(axis=1) / TRIALS, 3).tolist()}")

@@ -15,7 +15,8 @@
   (drafter-history page, DSpark acceptance label) within 4 sigma.
 - Special cases: q = p always accepts the first candidate; a one-hot p makes
   sequential rejection take the greedy path.
-- REJECT_PATH on a fixed tree with siblings at two depths: its joint law of
+- REJECT_PATH on a fixed tree with siblings at two depths (and on the same
+  tree with two children of the root sharing a token): its joint law of
   (stop node, next token) over 1e6 seeded trials passes a chi-square test
   against the exact table summed over every accept pattern of the seven
   candidate nodes (`exact_paths.py`, written from the mode's definition); the
@@ -393,20 +394,24 @@ def test_workload_inputs_run_through_oracle(oracle):
 # per-path rejection on a tree with siblings: exact enumeration
 # ----------------------------------------------------------------------------
 
-FIXED_SEED = 1911  # every node of the fixed tree stops the walk in at least 6% of trials
+# every node of each fixed tree stops the walk in at least 6% of trials; the
+# second tree gives two children of the root the same token (each is tested on
+# its own uniform)
+FIXED_CASES = {"distinct tokens": (synth.FIXED_TREE_TOKENS, 1911),
+               "duplicate siblings": (synth.FIXED_TREE_TOKENS_DUP, 2759)}
 
 
-def fixed_tree_counts(verify, n_trials, seed, chunk=250_000):
-    """Counts of (stop node, next token) over seeded trials of the fixed tree;
+def fixed_tree_counts(verify, n_trials, seed, case="distinct tokens", chunk=250_000):
+    """Counts of (stop node, next token) over seeded trials of a fixed tree;
     `verify(inp)` returns the verification outputs of one batch of trials."""
-    lp, lq, dft_row = synth.fixed_tree_logits(FIXED_SEED)
+    tokens, lseed = FIXED_CASES[case]
+    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens)
     rng = np.random.default_rng(seed)
     T, V = lp.shape
     counts = np.zeros((T, V), np.int64)
     for start in range(0, n_trials, chunk):
         B = min(chunk, n_trials - start)
-        inp = synth.make_fixed_tree_trials(rng, B, synth.FIXED_TREE_PARENTS,
-                                           synth.FIXED_TREE_TOKENS, lp, lq, dft_row)
+        inp = synth.make_fixed_tree_trials(rng, B, synth.FIXED_TREE_PARENTS, tokens, lp, lq, dft_row)
         res = verify(inp)
         stop = res["acc_path"][np.arange(B), res["acc_len"]]
         np.add.at(counts, (stop, res["next_token"]), 1)
@@ -422,14 +427,16 @@ def table_pvalue(counts, table):
     return _chi2_pvalue(counts[nz], table[nz] / table[nz].sum())
 
 
-def fixed_tree_tables():
-    lp, lq, dft_row = synth.fixed_tree_logits(FIXED_SEED)
-    return {v: per_path_table(synth.FIXED_TREE_PARENTS, synth.FIXED_TREE_TOKENS, lp, lq,
-                              dft_row, v) for v in VARIANTS}
+def fixed_tree_tables(case="distinct tokens"):
+    tokens, lseed = FIXED_CASES[case]
+    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens)
+    return {v: per_path_table(synth.FIXED_TREE_PARENTS, tokens, lp, lq, dft_row, v)
+            for v in VARIANTS}
 
 
-def test_reject_path_tree_matches_exact_enumeration(oracle):
-    tables = fixed_tree_tables()
+@pytest.mark.parametrize("case", list(FIXED_CASES))
+def test_reject_path_tree_matches_exact_enumeration(oracle, case):
+    tables = fixed_tree_tables(case)
     exact = tables["exact"]
     assert abs(exact.sum() - 1.0) < 1e-12
     assert exact.sum(axis=1).min() > 0.06  # every node is a stop node in the sample
@@ -441,7 +448,7 @@ def test_reject_path_tree_matches_exact_enumeration(oracle):
                              tr["n_nodes"], tr["parent"], tr["token"], tr["depth"],
                              inp["u_node"], inp["u_final"])
 
-    counts = fixed_tree_counts(run, 1_000_000, seed=1912)
+    counts = fixed_tree_counts(run, 1_000_000, seed=1912, case=case)
     assert table_pvalue(counts, exact) >= 1e-3
     for v in VARIANTS[1:]:
         assert table_pvalue(counts, tables[v]) < 1e-3, v

@@ -320,6 +320,7 @@ def make_two_level_trials(rng: np.random.Generator, B: int, lp0: np.ndarray, lq0
 # nodes 1..7 and their tokens (vocabulary of 6); nodes 0, 1, 2 and 4 have children
 FIXED_TREE_PARENTS = (0, 0, 0, 1, 1, 2, 4)
 FIXED_TREE_TOKENS = (0, 1, 2, 3, 4, 0, 5)
+FIXED_TREE_TOKENS_DUP = (0, 0, 2, 3, 4, 0, 5)  # nodes 1 and 2: the same token under the root
 
 
 def make_fixed_tree_trials(rng: np.random.Generator, B: int, cand_parent, cand_token,
@@ -352,7 +353,7 @@ def make_fixed_tree_trials(rng: np.random.Generator, B: int, cand_parent, cand_t
 FIXED_TREE_DFT_ROW = (0, 1, 2, -1, 3, -1, -1, -1)
 
 
-def fixed_tree_logits(seed: int) -> tuple:
+def fixed_tree_logits(seed: int, tokens=FIXED_TREE_TOKENS) -> tuple:
     """Logits rows of the fixed tree: target row of every node ~ N(0, 1.5^2),
     draft row of each node with children = its target row + N(0, 1), with each
     child's token raised by 0.5 in its parent's draft row (drafted tokens are
@@ -364,6 +365,6 @@ def fixed_tree_logits(seed: int) -> tuple:
     for node, r in enumerate(FIXED_TREE_DFT_ROW):
         if r >= 0:
             lq[r] = lp[node] + rng.standard_normal(6).astype(np.float32)
-    for par, tok in zip(FIXED_TREE_PARENTS, FIXED_TREE_TOKENS):
+    for par, tok in zip(FIXED_TREE_PARENTS, tokens):
         lq[FIXED_TREE_DFT_ROW[par], tok] += np.float32(0.5)
     return lp, lq, np.asarray(FIXED_TREE_DFT_ROW, np.int32)
