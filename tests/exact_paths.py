@@ -65,3 +65,52 @@ def per_path_table(parent, token, lp, lq, dft_row, variant="exact"):
             dist = p[s]
         table[s] += w * dist
     return table
+
+
+RECURSIVE_VARIANTS = ("exact", "draw_from_p", "reverse_order", "no_residual_update", "root_rows")
+
+
+def recursive_table(parent, token, lp, lq, dft_row, variant="exact"):
+    """(T, V) table of P(stop node, next token) under sequential rejection
+    ([ResiSpec] section 4, with the library's readings): the children of the
+    current node s are tested in node-index order against p', which starts as
+    p_s; child x is accepted with probability min(1, p'(x) / q_s(x)) and the
+    walk moves to it; each rejection sets p' <- norm(max(0, p' - q_s)); with no
+    child left the next token is drawn from p' (from p_s at a leaf).  The
+    process follows one path, so the table is a sum over the tree's nodes and
+    the number of rejections before each acceptance.  Variants: the final draw
+    from p_s, children tested in reverse order, p' never updated, every node's
+    residual built from the root's rows."""
+    assert variant in RECURSIVE_VARIANTS
+    par = [-1] + [int(x) for x in parent]
+    tok = [-1] + [int(x) for x in token]
+    T = len(par)
+    p = softmax(np.asarray(lp, np.float64), axis=1)
+    q = softmax(np.asarray(lq, np.float64), axis=1)
+    V = p.shape[1]
+    children = [[c for c in range(1, T) if par[c] == s] for s in range(T)]
+    table = np.zeros((T, V))
+
+    def visit(s, prob):
+        ch = children[s]
+        if not ch:
+            table[s] += prob * p[s]
+            return
+        rows = 0 if variant == "root_rows" else s
+        pr, qq = p[rows].copy(), q[dft_row[rows]]
+        if variant == "reverse_order":
+            ch = ch[::-1]
+        rem = prob
+        for c in ch:
+            x = tok[c]
+            acc = min(1.0, pr[x] / qq[x]) if qq[x] > 0 else (1.0 if pr[x] > 0 else 0.0)
+            if acc > 0:
+                visit(c, rem * acc)
+            rem *= 1.0 - acc
+            if variant != "no_residual_update":
+                r = np.maximum(0.0, pr - qq)
+                pr = r / r.sum()
+        table[s] += rem * (p[s] if variant == "draw_from_p" else pr)
+
+    visit(0, 1.0)
+    return table

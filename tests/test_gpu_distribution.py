@@ -20,7 +20,9 @@ numbers.  Per case:
   token equals the oracle's, sequences with a near-tie on either side excepted
   (they are counted and must stay rare).
 Per-path rejection on a fixed tree with siblings at two depths (V = 6; also with
-two children of the root sharing a token), in the one-pass and the walk formulation: the joint law of (stop node, next token)
+two children of the root sharing a token), in the one-pass and the walk formulation,
+and sequential rejection on the same trees (with rows where five or six nodes
+can stop): the joint law of (stop node, next token)
 over 1e6 trials passes a chi-square test against the exact table summed over
 every accept pattern (tests/exact_paths.py), with the oracle's inputs and
 element-wise parity on the first call.
@@ -40,7 +42,8 @@ from scipy.special import softmax
 
 import oracle
 from tree_attention_verification_beam_amd import pipeline, synth
-from test_oracle_verify import FIXED_CASES, fixed_tree_counts, fixed_tree_tables, table_pvalue
+from test_oracle_verify import (FIXED_CASES, RECURSIVE_CASES, fixed_tree_counts, fixed_tree_tables,
+                                recursive_tree_tables, table_pvalue)
 
 pytestmark = pytest.mark.gpu
 
@@ -190,6 +193,44 @@ def test_per_path_rejection_tree_matches_exact_enumeration(gpu, mode, case):
 
     counts = fixed_tree_counts(run, TRIALS, seed=1912, case=case)
     tables = fixed_tree_tables(case)
+    pv = table_pvalue(counts, tables["exact"])
+    log(f"  chi-square p-value against the exact table {pv:.4f}; stop nodes "
+        f"{np.round(counts.sum(axis=1) / TRIALS, 3).tolist()}")
+    assert pv >= 1e-3
+    for v, tab in tables.items():
+        if v != "exact":
+            assert table_pvalue(counts, tab) < 1e-3, v
+
+
+@pytest.mark.parametrize("case", list(RECURSIVE_CASES))
+@pytest.mark.parametrize("mode", ["reject_recursive", "reject_recursive_walk"])
+def test_sequential_rejection_tree_matches_exact_enumeration(gpu, mode, case):
+    log(f"case sequential rejection ({mode}) on a fixed 8-node tree ({case}), {TRIALS} trials at V=6")
+    first = [True]
+
+    def run(inp):
+        res = pipeline.Step(inp, mode=mode, device="cuda:0", with_kv=False).run()
+        assert res["status"] == 0, gpu.decode_status(res["status"])
+        if first[0]:
+            first[0] = False
+            tr = oracle.build_tree_explicit(inp["cand_parent"], inp["cand_token"],
+                                            inp["root_token"], inp["T_cap"])
+            for k in ("n_nodes", "parent", "token", "depth"):
+                assert np.array_equal(res[k], tr[k]), k
+            args = (inp["tgt"], inp["dft"], inp["dft_row"], tr["n_nodes"], tr["parent"],
+                    tr["token"], tr["depth"], inp["u_node"], inp["u_final"])
+            ora = (oracle.verify("reject_recursive", *args) if mode == "reject_recursive"
+                   else oracle.verify_reject_walk("reject_recursive", *args))
+            ok = (res["near_tie"] == 0) & (ora["near_tie"] == 0)
+            n_tie = int((~ok).sum())
+            log(f"  {n_tie} of {len(ok)} sequences with a near-tie")
+            assert n_tie <= len(ok) // 1000
+            for k in ("acc_len", "acc_path", "next_token", "decision"):
+                assert np.array_equal(res[k][ok], ora[k][ok]), k
+        return res
+
+    counts = fixed_tree_counts(run, TRIALS, seed=1913, case=case, cases=RECURSIVE_CASES)
+    tables = recursive_tree_tables(case)
     pv = table_pvalue(counts, tables["exact"])
     log(f"  chi-square p-value against the exact table {pv:.4f}; stop nodes "
         f"{np.round(counts.sum(axis=1) / TRIALS, 3).tolist()}")

@@ -23,6 +23,12 @@
   same counts fail against the tables of five plausible mistakes (ties to the
   highest index, no residual, survival without ancestors, the ratio inverted,
   the residual from the root's rows).
+- REJECT_RECURSIVE on the same fixed trees with fixed candidate tokens: the
+  joint law of (stop node, next token) over 1e6 trials passes a chi-square test
+  against the exact table of the mode's definition, summed over the one path
+  it follows (`exact_paths.recursive_table`); the counts fail against a final
+  draw from p_s, children tested in reverse order, p' never updated, and every
+  residual built from the root's rows.
 - Two positions: with rows that depend only on the token prefix (a root whose
   i.i.d. children each have their own i.i.d. children), the first emitted
   token follows p0 and, given first token x, the second follows p1[x]; the
@@ -35,7 +41,7 @@ from scipy import stats
 from scipy.special import softmax
 
 from tree_attention_verification_beam_amd import synth
-from exact_paths import VARIANTS, per_path_table
+from exact_paths import RECURSIVE_VARIANTS, VARIANTS, per_path_table, recursive_table
 
 
 # ----------------------------------------------------------------------------
@@ -397,15 +403,22 @@ def test_workload_inputs_run_through_oracle(oracle):
 # every node of each fixed tree stops the walk in at least 6% of trials; the
 # second tree gives two children of the root the same token (each is tested on
 # its own uniform)
-FIXED_CASES = {"distinct tokens": (synth.FIXED_TREE_TOKENS, 1911),
-               "duplicate siblings": (synth.FIXED_TREE_TOKENS_DUP, 2759)}
+FIXED_CASES = {"distinct tokens": (synth.FIXED_TREE_TOKENS, 1911, 0.5),
+               "duplicate siblings": (synth.FIXED_TREE_TOKENS_DUP, 2759, 0.5)}
+# sequential rejection: an acceptance probability of one cuts off the later
+# siblings, so some nodes are never the stop node; these rows keep five or six
+# nodes at 3% or more (the second reaches the root's residual draw after a
+# certain rejection of the duplicate)
+RECURSIVE_CASES = {"distinct tokens": (synth.FIXED_TREE_TOKENS, 1855, 0.0),
+                   "duplicate siblings": (synth.FIXED_TREE_TOKENS_DUP, 1388, 0.5)}
 
 
-def fixed_tree_counts(verify, n_trials, seed, case="distinct tokens", chunk=250_000):
+def fixed_tree_counts(verify, n_trials, seed, case="distinct tokens", chunk=250_000,
+                      cases=FIXED_CASES):
     """Counts of (stop node, next token) over seeded trials of a fixed tree;
     `verify(inp)` returns the verification outputs of one batch of trials."""
-    tokens, lseed = FIXED_CASES[case]
-    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens)
+    tokens, lseed, raise_drafted = cases[case]
+    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens, raise_drafted)
     rng = np.random.default_rng(seed)
     T, V = lp.shape
     counts = np.zeros((T, V), np.int64)
@@ -428,10 +441,17 @@ def table_pvalue(counts, table):
 
 
 def fixed_tree_tables(case="distinct tokens"):
-    tokens, lseed = FIXED_CASES[case]
-    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens)
+    tokens, lseed, raise_drafted = FIXED_CASES[case]
+    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens, raise_drafted)
     return {v: per_path_table(synth.FIXED_TREE_PARENTS, tokens, lp, lq, dft_row, v)
             for v in VARIANTS}
+
+
+def recursive_tree_tables(case="distinct tokens"):
+    tokens, lseed, raise_drafted = RECURSIVE_CASES[case]
+    lp, lq, dft_row = synth.fixed_tree_logits(lseed, tokens, raise_drafted)
+    return {v: recursive_table(synth.FIXED_TREE_PARENTS, tokens, lp, lq, dft_row, v)
+            for v in RECURSIVE_VARIANTS}
 
 
 @pytest.mark.parametrize("case", list(FIXED_CASES))
@@ -451,6 +471,26 @@ def test_reject_path_tree_matches_exact_enumeration(oracle, case):
     counts = fixed_tree_counts(run, 1_000_000, seed=1912, case=case)
     assert table_pvalue(counts, exact) >= 1e-3
     for v in VARIANTS[1:]:
+        assert table_pvalue(counts, tables[v]) < 1e-3, v
+
+
+@pytest.mark.parametrize("case", list(RECURSIVE_CASES))
+def test_reject_recursive_tree_matches_exact_enumeration(oracle, case):
+    tables = recursive_tree_tables(case)
+    exact = tables["exact"]
+    assert abs(exact.sum() - 1.0) < 1e-12
+    assert (exact.sum(axis=1) >= 0.03).sum() >= 5  # five or more stop nodes in the sample
+
+    def run(inp):
+        tr = oracle.build_tree_explicit(inp["cand_parent"], inp["cand_token"],
+                                        inp["root_token"], inp["T_cap"])
+        return oracle.verify("reject_recursive", inp["tgt"], inp["dft"], inp["dft_row"],
+                             tr["n_nodes"], tr["parent"], tr["token"], tr["depth"],
+                             inp["u_node"], inp["u_final"])
+
+    counts = fixed_tree_counts(run, 1_000_000, seed=1913, case=case, cases=RECURSIVE_CASES)
+    assert table_pvalue(counts, exact) >= 1e-3
+    for v in RECURSIVE_VARIANTS[1:]:
         assert table_pvalue(counts, tables[v]) < 1e-3, v
 
 

@@ -353,11 +353,12 @@ def make_fixed_tree_trials(rng: np.random.Generator, B: int, cand_parent, cand_t
 FIXED_TREE_DFT_ROW = (0, 1, 2, -1, 3, -1, -1, -1)
 
 
-def fixed_tree_logits(seed: int, tokens=FIXED_TREE_TOKENS) -> tuple:
+def fixed_tree_logits(seed: int, tokens=FIXED_TREE_TOKENS, raise_drafted: float = 0.5) -> tuple:
     """Logits rows of the fixed tree: target row of every node ~ N(0, 1.5^2),
     draft row of each node with children = its target row + N(0, 1), with each
     child's token raised by 0.5 in its parent's draft row (drafted tokens are
-    the draft's likely ones).  Returns (lp (8, 6), lq (4, 6), dft_row)."""
+    the draft's likely ones; `raise_drafted` sets the amount).  Returns
+    (lp (8, 6), lq (4, 6), dft_row)."""
     rng = np.random.default_rng(seed)
     T = len(FIXED_TREE_PARENTS) + 1
     lp = (1.5 * rng.standard_normal((T, 6))).astype(np.float32)
@@ -366,5 +367,5 @@ def fixed_tree_logits(seed: int, tokens=FIXED_TREE_TOKENS) -> tuple:
         if r >= 0:
             lq[r] = lp[node] + rng.standard_normal(6).astype(np.float32)
     for par, tok in zip(FIXED_TREE_PARENTS, tokens):
-        lq[FIXED_TREE_DFT_ROW[par], tok] += np.float32(0.5)
+        lq[FIXED_TREE_DFT_ROW[par], tok] += np.float32(raise_drafted)
     return lp, lq, np.asarray(FIXED_TREE_DFT_ROW, np.int32)
