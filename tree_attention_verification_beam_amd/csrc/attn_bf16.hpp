@@ -356,13 +356,10 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
 
   // ---------------------------------------------------------------- state
   f32x4 acc[QT][DT];
-  // one key group: the row sums of P come from one more MFMA per chunk against
-  // an all-ones operand, complete in every lane (the same bf16 P as P V)
-  constexpr bool kMfmaSum = KG == 1;
-  f32x4 acc_l[QT];
-  bf16x8 ones;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) ones[e] = (bf16_t)1.0f;
+  // l_run: each lane's fp32 sum of its own exponentials (before bf16 rounding);
+  // the 4 lane groups holding a query are added after the key loop.  An extra
+  // MFMA per chunk against an all-ones operand gives the same sums complete in
+  // every lane, but the kernel ran slower with it on every plan.
   float m_run[QT], l_run[QT];
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
@@ -370,7 +367,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
     l_run[i] = 0.0f;
 #pragma unroll
     for (int d = 0; d < DT; ++d) acc[i][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_l[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
   auto store_tile = [&](const bf16x8 (&kr)[K_UNITS], const bf16x8 (&vr)[VK], int stage) {
@@ -531,7 +527,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
               const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
               pf[j][i][4 * st + e] = (bf16_t)pv;
               pmax = max(pmax, __builtin_bit_cast(uint32_t, pv));
-              if constexpr (!kMfmaSum) psum[i] += pv;
+              psum[i] += pv;
             }
         grow[i] = __builtin_amdgcn_ballot_w64(pmax > kGrowBits || m_run[i] == -INFINITY) != 0ull;
         any_grow = any_grow || grow[i];
@@ -554,7 +550,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           const float alpha =
               (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
           l_run[i] *= alpha;
-          acc_l[i] *= alpha;
 #pragma unroll
           for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
           m_run[i] = m_new;
@@ -568,14 +563,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
               for (int e = 0; e < 4; ++e) {
                 const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
                 pf[j][i][4 * st + e] = (bf16_t)pv;
-                if constexpr (!kMfmaSum) psum[i] += pv;
+                psum[i] += pv;
               }
         }
       }
-      if constexpr (!kMfmaSum) {
 #pragma unroll
-        for (int i = 0; i < QT; ++i) l_run[i] += psum[i];
-      }
+      for (int i = 0; i < QT; ++i) l_run[i] += psum[i];
     } else {
       // online softmax in exp2 form; lane owns query l16 and, in chunk j, keys
       // wkey0 + 32 j + 8 lg + 4 (st ^ h) + e.  A row maximum moves only when some
@@ -609,7 +602,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
           const float alpha =
               (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_run[i] - m_new);
           l_run[i] *= alpha;
-          acc_l[i] *= alpha;
 #pragma unroll
           for (int d = 0; d < DT; ++d) acc[i][d] *= alpha;
           m_run[i] = m_new;
@@ -627,9 +619,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
             for (int e = 0; e < 4; ++e) {
               const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[j][i][st][e], c, nmu));
               pf[j][i][4 * st + e] = (bf16_t)pv;
-              if constexpr (!kMfmaSum) psum += pv;
+              psum += pv;
             }
-        if constexpr (!kMfmaSum) l_run[i] += psum;
+        l_run[i] += psum;
       }
     }
   };
@@ -660,10 +652,6 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
         }
 #pragma unroll
         for (int i = 0; i < QT; ++i) acc[i][d] = mfma16x16x32(vf, pf[j][i], acc[i][d]);
-      }
-      if constexpr (kMfmaSum) {
-#pragma unroll
-        for (int i = 0; i < QT; ++i) acc_l[i] = mfma16x16x32(ones, pf[j][i], acc_l[i]);
       }
     }
   };
@@ -774,16 +762,12 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void k_attn_bf16(AttnArgs
   }
 
   // ---------------------------------------------------------------- combine lanes
-  // the MFMA row sums are complete in every lane; the VALU ones are partial
-  // sums of the 4 lane groups of a query over their own keys
+  // each lane holds the partial sum of its own keys; the 4 lane groups of a
+  // query (lanes l, l ^ 16, l ^ 32, l ^ 48) add theirs
 #pragma unroll
   for (int i = 0; i < QT; ++i) {
-    if constexpr (kMfmaSum) {
-      l_run[i] = acc_l[i][0];
-    } else {
-      l_run[i] += partner_f32<4>(l_run[i]);
-      l_run[i] += partner_f32<5>(l_run[i]);
-    }
+    l_run[i] += partner_f32<4>(l_run[i]);
+    l_run[i] += partner_f32<5>(l_run[i]);
   }
 
   // ---------------------------------------------------------------- combine key groups

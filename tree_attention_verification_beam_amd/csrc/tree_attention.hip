@@ -19,10 +19,8 @@
 // straight into LDS as they lie in memory and the V^T operand comes from
 // transposing LDS reads), computes S^T = K Q^T with v_mfma_f32_16x16x32_bf16 so
 // that each lane owns one query row, runs the online softmax in fp32 in exp2
-// form, and accumulates O^T = V^T P^T with the same MFMA (and, when every wave
-// sees all keys of a tile, the row sums of P as one more MFMA against an
-// all-ones operand, which leaves the softmax only its exponentials and the
-// running maximum on the VALU).  When few rows exist
+// form (row sums of P in fp32 per lane, added across lanes after the key
+// loop), and accumulates O^T = V^T P^T with the same MFMA.  When few rows exist
 // (no GQA, small trees) the waves split each key tile instead (KG key groups)
 // and combine through LDS at the end.  The running maximum is only moved when
 // a score exceeds it by more than 2^8, so most tiles skip the rescale of the
