@@ -138,8 +138,8 @@ def test_large_batch_large_vocab(gpu):
 
 def test_attention_repeated_launches_match(gpu):
     """Forty launches of one attention call whose plan has two query tiles per
-    wave, two tiles of loads in flight and two-tile context splits (the tree
-    keys fall in the first tile of the last split).  Every launch must match
+    wave, two 4-wave row blocks of direct loads (196 rows) and two-tile context
+    splits (the tree keys fall in the first tile of the last split).  Every launch must match
     the oracle: a wrongly unmasked tree key shows up as an intermittent error,
     so one launch is not enough."""
     inp = synth.make_inputs(4, 100, B_override=1, ctx_override=3000)

@@ -4,7 +4,9 @@ The context of a (sequence, KV head) is split over workgroups so that the grid
 covers the CUs; a merge kernel then combines the (max, sum, O) partials.  The
 shapes below make the plan choose 1, 2, 4, 21 and 32 splits (the last two with
 two and with one key group), for 1024 (sequence, head) streams 4-wave groups,
-and 24 splits of the 4-wave GQA plan that loads its tiles straight into LDS;
+24 splits of the 4-wave GQA plan that loads its tiles straight into LDS, one
+8-wave row block of register-staged tiles (5 query tiles) and two 4-wave
+direct-load row blocks (9 query tiles);
 each is compared with the oracle within 1e-2 of the largest output, with
 ragged contexts where B > 1.  The same GQA plan is also run without splits on
 the 70B shape and on ranges shorter than one key tile.
@@ -30,6 +32,12 @@ CASES = {
     "1024 streams": (32, 32, 32, [40 + 7 * i for i in range(32)]),
     # 272 rows per KV head: the 4-wave plan whose tiles go straight to LDS
     "24 splits, GQA direct loads": (1, 32, 2, [3000]),
+    # 68 rows per KV head (5 query tiles): one 8-wave row block of
+    # register-staged tiles, two query tiles per wave
+    "one 8-wave row block": (2, 8, 2, [2000, 1500]),
+    # 136 rows per KV head (9 query tiles): two 4-wave row blocks of direct
+    # loads, the second with one live query tile
+    "two direct-load row blocks": (2, 16, 2, [2000, 1500]),
 }
 
 

@@ -85,15 +85,18 @@ AttnPlan make_plan(int B, int T_cap, int H, int Hkv, int D, int max_ctx) {
     // the stream rate) and at most 32 rows: 4-wave groups with two tiles of
     // loads in flight stream faster
     if (nq <= 2 && (long)B * Hkv >= 4L * kNumCU) { p.NW = 4; p.PF = 2; }
-  } else if (nq <= 16) {
+  } else if (nq <= 8 || (nq <= 16 && D != 128)) {
     // one row block: two query tiles per wave, two tiles of loads in flight
     p.KG = 1; p.QT = 2; p.PF = 2;
   } else {
-    // many rows (wide GQA groups): 128-row blocks of 4 waves with two query
-    // tiles each read the same key range, two workgroups per CU; at D = 128
-    // the tiles go straight to LDS, which frees the staging registers and the
-    // stores from the waves, and the scores of the next tile run beside the
-    // softmax and P V of this one
+    // many rows (wide GQA groups; at D = 128 from 9 query tiles on): 128-row
+    // blocks of 4 waves with two query tiles each read the same key range, two
+    // workgroups per CU; at D = 128 the tiles go straight to LDS, which frees
+    // the staging registers and the stores from the waves, and the scores of
+    // the next tile run beside the softmax and P V of this one.  With 9 to 16
+    // query tiles this beats one 8-wave block of register-staged tiles (196
+    // rows, 32k keys: 157 -> 149 us), and an 8-wave block of direct loads
+    // (161 us).
     p.NW = 4; p.KG = 1; p.QT = 2; p.PF = 2;
     if (D == 128) p.NS = 2;
   }
